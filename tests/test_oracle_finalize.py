@@ -1,0 +1,385 @@
+"""Pins for the finalize oracle (CPU only).
+
+The oracle is checked against hand-worked fixtures, exact rational
+arithmetic, an independent scatter formulation, invariants the pages imply
+(pure gather, identical rows, NaN padding never read, packed == bf16-rounded
+fp32 weights, rsf 1.0 neutral) and library routines (torch rms_norm and
+casts). Each test is built so that a plausible slip in the oracle (a dropped
+term, a wrong sign or index, transposed operands, rsf on the wrong operand,
+double rounding) fails at least one of them.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import finalize as O
+from oracle import formats as F
+from combine_moe_finalize_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def f32_bits_to_bf16(vals):
+    """bf16 bits of exactly representable float values (via torch)."""
+    a = np.array([float("nan") if v == "nan" else v for v in vals], dtype=np.float32)
+    return W.to_bf16_bits(a)
+
+
+def frac_bf16(q: Fraction) -> float:
+    """Exact nearest-even rounding of a rational to bf16, as a float."""
+    if q == 0:
+        return 0.0
+    s = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - 7)
+    m = a / ulp
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return float(s * n * ulp)
+
+
+# ------------------------------------------------------------ golden cases
+@pytest.fixture(scope="module")
+def tiny():
+    g = load_golden("finalize_tiny.json")
+    g2 = np.stack([f32_bits_to_bf16(r) for r in g["gemm2_out"]])
+    idx = np.array(g["expanded_idx_to_permuted_idx"], dtype=np.int32)
+    w = np.array(g["weights"], dtype=np.float32)
+    sh = np.stack([f32_bits_to_bf16(r) for r in g["shared"]])
+    return g, g2, idx, w, sh
+
+
+def test_golden_fixture_is_self_consistent(tiny):
+    # the hand-worked expectations, re-derived with exact rationals
+    g, g2, idx, w, sh = tiny
+    rsf = Fraction(g["rsf"])
+    for t in range(idx.shape[0]):
+        for h in range(g["H"]):
+            q = sum(Fraction(float(w[t, k])) * rsf * Fraction(g["gemm2_out"][idx[t, k]][h])
+                    for k in range(g["top_k"])) + Fraction(g["shared"][t][h])
+            assert frac_bf16(q) == g["expected_out"][t][h]
+
+
+@pytest.mark.parametrize("mode", ["truth", "mirror"])
+def test_golden_tiny_finalize(tiny, mode):
+    g, g2, idx, w, sh = tiny
+    fn = O.finalize_truth if mode == "truth" else O.finalize_mirror
+    out, flag = fn(g2, idx, weights_f32=w, shared=sh, rsf=g["rsf"])
+    assert flag == 0
+    assert np.array_equal(F.bf16_to_f64(out), np.array(g["expected_out"], dtype=np.float64))
+    out, _ = fn(g2, idx, weights_f32=w, shared=None, rsf=1.0)
+    assert np.array_equal(F.bf16_to_f64(out),
+                          np.array(g["expected_out_no_shared_rsf1"], dtype=np.float64))
+
+
+def test_golden_packed_decode():
+    g = load_golden("packed_routing.json")
+    words = np.array([int(h, 16) for h in g["words_hex"]], dtype=np.uint32).view(np.int32)
+    ids, w = O.decode_packed(words)
+    assert list(ids) == g["expert_ids"]
+    assert list(w.astype(np.float64)) == g["weights"]
+
+
+def test_golden_ue8m0_quant():
+    g = load_golden("ue8m0_quant.json")
+    e = F.ue8m0_exponent(np.array(g["amax"], dtype=np.float64))
+    assert list(e) == g["exponent"]
+    assert list(F.ue8m0_code(e)) == g["scale_byte"]
+    head = g["block_values_head"]
+    row = np.array(head + [g["block_rest"]] * (128 - len(head)), dtype=np.float32)
+    codes, scales, ex = O.quant_ue8m0(W.to_bf16_bits(row)[None, :])
+    assert ex[0, 0] == g["block_exponent"] and scales[0, 0] == g["block_exponent"] + 127
+    assert [f"{c:02X}" for c in codes[0, :len(head)]] == g["block_codes_head_hex"]
+    assert np.all(codes[0, len(head):] == 0)
+
+
+# -------------------------------------------------- exact rational brute force
+def test_config0_truth_equals_exact_rational():
+    wl = W.config_workload(0)
+    out, flag = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                                 shared=wl.shared, rsf=wl.rsf)
+    assert flag == 0
+    got = F.bf16_to_f64(out)
+    rsf32 = np.float32(wl.rsf)
+    for t in range(wl.T):
+        wq = [Fraction(float(np.float32(wl.weights[t, k] * rsf32))) for k in range(wl.top_k)]
+        rows = [F.bf16_to_f64(wl.gemm2_out[wl.idx[t, k]]) for k in range(wl.top_k)]
+        sh = F.bf16_to_f64(wl.shared[t])
+        for h in range(wl.H):
+            q = sum(wq[k] * Fraction(rows[k][h]) for k in range(wl.top_k)) + Fraction(sh[h])
+            assert got[t, h] == frac_bf16(q), (t, h)
+
+
+def test_scatter_formulation_matches_gather():
+    """Loop over permuted rows (the producer's order) and scatter into
+    tokens; equal to the token-major gather after one rounding."""
+    wl = W.make_workload(40, 256, 16, 4, rsf=2.5, seed=11, pad=16)
+    out, _ = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                              shared=wl.shared, rsf=wl.rsf)
+    owner = {}
+    for t in range(wl.T):
+        for k in range(wl.top_k):
+            owner[int(wl.idx[t, k])] = (t, k)
+    acc = F.bf16_to_f64(wl.shared).copy()
+    for r in range(wl.P):
+        if r not in owner:
+            continue
+        t, k = owner[r]
+        wq = float(np.float32(wl.weights[t, k] * np.float32(wl.rsf)))
+        acc[t] += wq * F.bf16_to_f64(wl.gemm2_out[r])
+    assert np.array_equal(F.bf16_bits(acc), out)
+
+
+# -------------------------------------------------------------- invariants
+@pytest.mark.parametrize("mode", ["truth", "mirror"])
+def test_pure_gather(mode):
+    wl = W.make_workload(64, 512, 32, 1, rsf=1.0, seed=5, with_shared=False)
+    fn = O.finalize_truth if mode == "truth" else O.finalize_mirror
+    out, flag = fn(wl.gemm2_out, wl.idx, weights_f32=np.ones_like(wl.weights), rsf=1.0)
+    ref = wl.gemm2_out[wl.idx[:, 0]]
+    assert flag == 0
+    # +0 / -0 compare equal; every other bit must match
+    assert np.array_equal(F.bf16_to_f64(out), F.bf16_to_f64(ref))
+
+
+@pytest.mark.parametrize("mode", ["truth", "mirror"])
+def test_identical_rows_reproduce_the_row(mode):
+    wl = W.make_workload(32, 256, 16, 8, rsf=1.0, seed=6, with_shared=False, pad=32)
+    g2 = wl.gemm2_out.copy()
+    T = wl.T
+    base = g2[wl.idx[:, 0]]                       # one row per token
+    for k in range(wl.top_k):
+        g2[wl.idx[:, k]] = base                   # all top_k rows identical
+    fn = O.finalize_truth if mode == "truth" else O.finalize_mirror
+    out, _ = fn(g2, wl.idx, weights_f32=wl.weights, rsf=1.0)
+    assert np.array_equal(F.bf16_to_f64(out), F.bf16_to_f64(base))
+
+
+def test_nan_padding_never_reaches_output():
+    for cfg, T in [(0, 1), (1, 16), (2, 256)]:
+        wl = W.config_workload(cfg, T)
+        assert np.isnan(F.bf16_to_f64(wl.gemm2_out)).any()   # padding exists
+        out, flag = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                                     shared=wl.shared, rsf=wl.rsf)
+        assert flag == 0 and np.isfinite(F.bf16_to_f64(out)).all()
+
+
+def test_rsf_one_is_neutral_and_scales_only_routed():
+    wl = W.config_workload(1, 8)
+    a, _ = O.finalize_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                             shared=wl.shared, rsf=1.0)
+    # rsf = 1.0 equals the definition with the raw fp32 weights
+    w1 = O.effective_weights(wl.weights, None, 1.0)
+    assert np.array_equal(w1, wl.weights)
+    b, _ = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                            shared=wl.shared, rsf=1.0)
+    assert np.max(np.abs(F.bf16_to_f64(a) - F.bf16_to_f64(b)) /
+                  np.maximum(np.abs(F.bf16_to_f64(b)), 1e-30)) <= 2 ** -7
+    # zero routing weights: the output is the shared expert, whatever rsf is
+    z, _ = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=np.zeros_like(wl.weights),
+                            shared=wl.shared, rsf=2.5)
+    assert np.array_equal(z, wl.shared)
+    # rsf scales the routed sum: with no shared output, rsf 2 doubles it exactly
+    o1, _ = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wl.weights, rsf=1.0)
+    o2, _ = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wl.weights, rsf=2.0)
+    assert np.array_equal(F.bf16_to_f64(o2), 2 * F.bf16_to_f64(o1))
+    # and it must actually change the result
+    assert not np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("mode", ["truth", "mirror"])
+def test_doubling_is_exact(mode):
+    wl = W.config_workload(1, 4)
+    fn = O.finalize_truth if mode == "truth" else O.finalize_mirror
+    a, _ = fn(wl.gemm2_out, wl.idx, weights_f32=wl.weights, shared=wl.shared, rsf=1.25)
+    sh2 = W.to_bf16_bits(2 * F.bf16_to_f32(wl.shared))
+    b, _ = fn(wl.gemm2_out, wl.idx, weights_f32=wl.weights, shared=sh2, rsf=2.5)
+    assert np.array_equal(F.bf16_to_f64(b), 2 * F.bf16_to_f64(a))
+
+
+@pytest.mark.parametrize("mode", ["truth", "mirror"])
+def test_packed_equals_bf16_rounded_unpacked(mode):
+    wl = W.config_workload(2)
+    fn = O.finalize_truth if mode == "truth" else O.finalize_mirror
+    wl_sub = slice(0, 64)
+    idx = wl.idx[wl_sub]
+    sh = wl.shared[wl_sub]
+    p, _ = fn(wl.gemm2_out, idx, packed=wl.packed[wl_sub], shared=sh, rsf=wl.rsf)
+    wr = F.bf16_to_f32(W.to_bf16_bits(wl.weights[wl_sub]))   # torch-rounded
+    u, _ = fn(wl.gemm2_out, idx, weights_f32=wr, shared=sh, rsf=wl.rsf)
+    assert np.array_equal(p, u)
+    # discriminating: the genuine fp32 weights give a different result, so a
+    # path that silently drops to bf16 weights (or reads fp32 as bf16) shows
+    f, _ = fn(wl.gemm2_out, idx, weights_f32=wl.weights[wl_sub], shared=sh, rsf=wl.rsf)
+    assert not np.array_equal(p, f)
+
+
+def test_decode_roundtrip_all_ids():
+    rng = np.random.default_rng(7)
+    ids = np.arange(1 << 16, dtype=np.int64)
+    w = rng.uniform(-4, 4, ids.size).astype(np.float32)
+    words = W.pack_routing(ids.astype(np.uint32), w)
+    dids, dw = O.decode_packed(words)
+    assert np.array_equal(dids, ids)
+    ref = torch.from_numpy(w).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(dw, ref)
+    # reading fp32 weights as if they were packed words does not give them back
+    _, bad = O.decode_packed(w.view(np.int32))
+    assert not np.array_equal(bad, w)
+
+
+def test_layout_invariance():
+    """Relocating expert segments and shuffling rows within them (the map
+    updated to match) leaves the result bitwise unchanged."""
+    wl = W.make_workload(48, 256, 16, 4, rsf=2.5, seed=9, pad=8)
+    ref, _ = O.finalize_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                               shared=wl.shared, rsf=wl.rsf)
+    rng = np.random.default_rng(10)
+    newpos = rng.permutation(wl.P + 37)[:wl.P]          # new home of each row
+    g2 = np.full((wl.P + 37, wl.H), W.NAN_BF16, dtype=np.uint16)
+    g2[newpos] = wl.gemm2_out
+    idx = newpos[wl.idx].astype(np.int32)
+    out, _ = O.finalize_mirror(g2, idx, weights_f32=wl.weights, shared=wl.shared, rsf=wl.rsf)
+    assert np.array_equal(out, ref)
+    outt, _ = O.finalize_truth(g2, idx, weights_f32=wl.weights, shared=wl.shared, rsf=wl.rsf)
+    reft, _ = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                               shared=wl.shared, rsf=wl.rsf)
+    assert np.array_equal(outt, reft)
+
+
+def test_index_rules_skip_and_flag():
+    wl = W.make_workload(16, 128, 8, 4, rsf=2.5, seed=12, pad=16)
+    idx = wl.idx.copy()
+    idx[3, 1] = -1                  # expert not local: slot skipped
+    idx[5, 2] = wl.P + 3            # out of range: skipped and flagged
+    w = wl.weights.copy()
+    for mode in (O.finalize_truth, O.finalize_mirror):
+        out, flag = mode(wl.gemm2_out, idx, weights_f32=w, shared=wl.shared, rsf=wl.rsf)
+        assert flag == O.ERR_INDEX_OUT_OF_RANGE
+        wz = w.copy()
+        wz[3, 1] = 0.0
+        wz[5, 2] = 0.0
+        ref, f2 = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wz,
+                                   shared=wl.shared, rsf=wl.rsf)
+        assert f2 == 0
+        assert np.array_equal(F.bf16_to_f64(out), F.bf16_to_f64(ref))
+    _, flag = O.finalize_truth(wl.gemm2_out, np.where(idx >= wl.P, 0, idx),
+                               weights_f32=w, shared=wl.shared, rsf=wl.rsf)
+    assert flag == 0
+
+
+def test_mirror_within_two_ulp_of_truth():
+    wl = W.config_workload(1, 64)
+    m, _ = O.finalize_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                             shared=wl.shared, rsf=wl.rsf)
+    t, _ = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                            shared=wl.shared, rsf=wl.rsf)
+    mt, tt = F.bf16_to_f64(m), F.bf16_to_f64(t)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(tt))[1] - 8)
+    assert np.all(np.abs(mt - tt) <= 2 * ulp + 1e-30)
+    # the two modes differ somewhere (fp32 vs fp64 sums), but rarely
+    assert np.mean(m != t) < 0.01
+
+
+# ---------------------------------------------------------- residual + RMSNorm
+def test_residual_out_is_single_rounding_of_shared_like_term():
+    wl = W.config_workload(3, 16)
+    ro, _, _ = O.finalize_residual_rmsnorm_truth(
+        wl.gemm2_out, wl.idx, weights_f32=wl.weights, shared=None, rsf=wl.rsf,
+        residual=wl.residual, gamma=wl.gamma, eps=wl.eps)
+    ref, _ = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                              shared=wl.residual, rsf=wl.rsf)
+    assert np.array_equal(ro, ref)
+
+
+def test_residual_out_exact_rational_tiny():
+    wl = W.make_workload(2, 64, 8, 4, rsf=2.5, seed=13, with_residual=True, pad=8)
+    ro, _, _ = O.finalize_residual_rmsnorm_truth(
+        wl.gemm2_out, wl.idx, weights_f32=wl.weights, shared=wl.shared, rsf=wl.rsf,
+        residual=wl.residual, gamma=wl.gamma, eps=wl.eps)
+    got = F.bf16_to_f64(ro)
+    rsf32 = np.float32(wl.rsf)
+    for t in range(wl.T):
+        for h in range(wl.H):
+            q = Fraction(float(F.bf16_to_f64(wl.shared[t, h]))) + \
+                Fraction(float(F.bf16_to_f64(wl.residual[t, h])))
+            for k in range(wl.top_k):
+                q += Fraction(float(np.float32(wl.weights[t, k] * rsf32))) * \
+                     Fraction(float(F.bf16_to_f64(wl.gemm2_out[wl.idx[t, k], h])))
+            assert got[t, h] == frac_bf16(q)
+
+
+def test_rmsnorm_matches_torch_rms_norm():
+    wl = W.config_workload(3, 16)
+    ro, normed, _ = O.finalize_residual_rmsnorm_truth(
+        wl.gemm2_out, wl.idx, weights_f32=wl.weights, shared=wl.shared, rsf=wl.rsf,
+        residual=wl.residual, gamma=wl.gamma, eps=wl.eps)
+    x = torch.from_numpy(F.bf16_to_f64(ro))
+    g = torch.from_numpy(F.bf16_to_f64(wl.gamma))
+    ref = torch.nn.functional.rms_norm(x, (wl.H,), weight=g,
+                                       eps=float(np.float32(wl.eps))).numpy()
+    got = F.bf16_to_f64(normed)
+    # torch result is fp64; one bf16 rounding apart at most
+    ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
+    assert np.all(np.abs(got - ref) <= 0.5 * ulp + 1e-300)
+
+
+def test_rmsnorm_constant_row_closed_form():
+    H = 256
+    for c in [1.0, -3.5, 0.0078125]:
+        x = W.to_bf16_bits(np.full((1, H), c, np.float32))
+        g = W.to_bf16_bits(np.linspace(0.5, 1.5, H).astype(np.float32))
+        eps = 1e-6
+        y = F.bf16_to_f64(O.rmsnorm_f64(x, g, eps))
+        cf = c / np.sqrt(c * c + np.float64(np.float32(eps)))
+        ref = F.bf16_to_f64(g) * cf
+        ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
+        assert np.all(np.abs(y - ref) <= 0.5 * ulp)
+
+
+# ------------------------------------------------------------------- quant
+def test_quant_block_bracket_and_reconstruction():
+    wl = W.make_workload(8, 1024, 16, 4, rsf=2.5, seed=14, log2_mag=(-8, 8), pad=16)
+    y, _ = O.finalize_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                             shared=None, rsf=wl.rsf)
+    codes, scales, e = O.quant_ue8m0(y)
+    yv = F.bf16_to_f64(y).reshape(wl.T, -1, 128)
+    amax = np.abs(yv).max(-1)
+    assert np.all(amax <= 448 * np.exp2(e)) and np.all(amax > 448 * np.exp2(e - 1))
+    assert np.array_equal(scales.astype(np.int64), e + 127)
+    dq = F.e4m3_decode(codes).reshape(wl.T, -1, 128) * np.exp2(e)[..., None]
+    # nearest-even E4M3: relative error <= 2^-4 for normals, abs <= 2^-10*2^e below
+    err = np.abs(dq - yv)
+    bound = np.maximum(np.abs(yv) * 2.0 ** -4, 2.0 ** -10 * np.exp2(e)[..., None])
+    assert np.all(err <= bound)
+    # each block's largest element lands at or above 224 (it exceeds 224
+    # before rounding, and 224 is an E4M3 value)
+    top = np.abs(F.e4m3_decode(codes).reshape(wl.T, -1, 128)).max(-1)
+    assert np.all(top >= 224) and np.all(top <= 448)
+
+
+def test_quant_zero_block_and_composition():
+    wl = W.make_workload(4, 256, 8, 2, rsf=2.5, seed=15, pad=8)
+    c1, s1, _ = O.finalize_quant_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                                        shared=wl.shared, rsf=wl.rsf)
+    y, _ = O.finalize_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                             shared=wl.shared, rsf=wl.rsf)
+    c2, s2, _ = O.quant_ue8m0(y)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    zc, zs, ze = O.quant_ue8m0(np.zeros((1, 128), np.uint16))
+    assert np.all(zc == 0) and zs[0, 0] == 0 and ze[0, 0] == -127
