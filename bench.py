@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X deferred MoE finalize (one GPU).
+
+One step = one call of the timed entry point over one batch of synthetic
+input already resident in HBM. The default workload is the prefill-size
+finalize with the FP8 / UE8M0 epilogue (T=8192 tokens, hidden 7168, 256
+experts, top_k 8, routed scaling factor 2.5, per-row magnitudes 2^U(-8,8)):
+the largest batch, where the path must run at HBM speed. Its call carries
+every step of the path: routing-weight load and scaling, index load, row
+gather, fp32 weighted reduce, shared-expert add, bf16 rounding and the 1x128
+UE8M0 / E4M3 quantization.
+
+Printed: one JSON line with
+  value      algorithmic GB/s of the whole step (bytes the method must move /
+             wall time per step, inputs resident),
+  roofline   the kernel's algorithmic bytes per launch / its average duration
+             from HIP events on the launch stream, against the 8 TB/s HBM peak;
+             `traffic` is the counter-measured HBM bytes per launch from the
+             committed rocprofv3 counter summary when it matches the current
+             kernel source, else null,
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload,
+  sweep      microseconds per call and GB/s for the other workload shapes
+             (decode T=1..256, packed vs fp32 routing, residual + RMSNorm),
+             kernel time from HIP events, warm (back-to-back) and cold
+             (after streaming a 1 GiB buffer through the caches).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "combine_moe_finalize_amd", "csrc", "finalize_kernels.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_quant_T8192_H7168_counters.json")
+
+
+# ------------------------------------------------------------ byte models
+def bytes_plain(T, H, k, shared=True):
+    return T * (2 * H * (k + (2 if shared else 1)) + 8 * k)
+
+
+def bytes_rmsnorm(T, H, k, shared=True):
+    return T * (2 * H * (k + (4 if shared else 3)) + 8 * k) + 2 * H
+
+
+def bytes_quant(T, H, k, shared=True):
+    return T * (2 * H * (k + (1 if shared else 0)) + H + H // 128 + 8 * k)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def counters_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------- utilities
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def upload(wl, torch, packed=False):
+    dev = "cuda:0"
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    kw = dict(gemm2_out=bf16(wl.gemm2_out),
+              expanded_idx_to_permuted_idx=torch.from_numpy(wl.idx).to(dev),
+              routed_scaling_factor=wl.rsf)
+    if packed:
+        kw["topk_packed"] = torch.from_numpy(wl.packed).to(dev)
+    else:
+        kw["topk_weights"] = torch.from_numpy(wl.weights).to(dev)
+    if wl.shared is not None:
+        kw["shared_out"] = bf16(wl.shared)
+    extra = {}
+    if wl.residual is not None:
+        extra = dict(residual=bf16(wl.residual), gamma=bf16(wl.gamma), eps=wl.eps)
+    return kw, extra
+
+
+def event_times_us(torch, fn, iters, flush=None):
+    """Per-call GPU time (HIP events on the current stream) of fn()."""
+    s = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for i in range(iters):
+        if flush is not None:
+            flush()
+        starts[i].record(s)
+        fn()
+        ends[i].record(s)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) * 1e3 for a, b in zip(starts, ends)])
+
+
+# --------------------------------------------------------------- CPU leg
+def cpu_baseline(wl, budget_s=15.0, chunk=256):
+    """The oracle (fp64 truth finalize + UE8M0 quant), single thread, on the
+    leading tokens of the workload until the time budget is spent."""
+    from oracle import finalize as O
+    done = 0
+    t0 = time.perf_counter()
+    while done < wl.T and time.perf_counter() - t0 < budget_s:
+        sl = slice(done, min(wl.T, done + chunk))
+        O.finalize_quant_truth(wl.gemm2_out, wl.idx[sl], weights_f32=wl.weights[sl],
+                               shared=wl.shared[sl], rsf=wl.rsf)
+        done = sl.stop
+    dt = time.perf_counter() - t0
+    gbs = bytes_quant(done, wl.H, wl.top_k) / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {wl.T} tokens of the same workload "
+                      f"(fp64 finalize + UE8M0/E4M3 quant, numpy, one thread), {dt:.1f} s"}
+
+
+# ----------------------------------------------------------------- sweep
+def sweep(torch, M, W, iters_small=200, iters_big=50):
+    flush_buf = torch.empty(1 << 29, dtype=torch.int16, device="cuda:0")   # 1 GiB
+
+    def flush():
+        flush_buf.fill_(1)
+
+    rows = []
+
+    def measure(name, T, H, k, nbytes, fn, iters):
+        for _ in range(5):
+            fn()
+        warm = event_times_us(torch, fn, iters)
+        cold = event_times_us(torch, fn, max(10, iters // 10), flush=flush)
+        rows.append({"case": name, "T": T, "H": H, "top_k": k,
+                     "us_warm_median": round(float(np.median(warm)), 3),
+                     "us_warm_p10": round(float(np.percentile(warm, 10)), 3),
+                     "us_warm_p90": round(float(np.percentile(warm, 90)), 3),
+                     "us_cold_median": round(float(np.median(cold)), 3),
+                     "gbs_warm": round(nbytes / (np.median(warm) * 1e-6) / 1e9, 1),
+                     "gbs_cold": round(nbytes / (np.median(cold) * 1e-6) / 1e9, 1)})
+        log(f"sweep {rows[-1]}")
+
+    wl = W.config_workload(0)
+    kw, _ = upload(wl, torch)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
+    measure("tiny", wl.T, wl.H, wl.top_k, bytes_plain(wl.T, wl.H, wl.top_k),
+            lambda: M.moe_finalize(**kw, out=out), iters_small)
+    for T in W.CONFIGS[1]["Ts"]:
+        wl = W.config_workload(1, T)
+        kw, _ = upload(wl, torch)
+        out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
+        measure("decode", T, wl.H, wl.top_k, bytes_plain(T, wl.H, wl.top_k),
+                lambda: M.moe_finalize(**kw, out=out), iters_small)
+    wl = W.config_workload(2)
+    for packed in (False, True):
+        kw, _ = upload(wl, torch, packed=packed)
+        out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
+        measure("packed" if packed else "fp32_weights", wl.T, wl.H, wl.top_k,
+                bytes_plain(wl.T, wl.H, wl.top_k), lambda: M.moe_finalize(**kw, out=out),
+                iters_small)
+    for T in W.CONFIGS[3]["Ts"]:
+        wl = W.config_workload(3, T)
+        kw, ex = upload(wl, torch)
+        ro = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
+        nm = torch.empty_like(ro)
+        measure("residual_rmsnorm", T, wl.H, wl.top_k, bytes_rmsnorm(T, wl.H, wl.top_k),
+                lambda: M.moe_finalize_residual_rmsnorm(**kw, **ex, residual_out=ro, normed=nm),
+                iters_big if T >= 1024 else iters_small)
+    n = 8192 * 8
+    pk = torch.from_numpy(W.config_workload(0).packed.reshape(-1).repeat(n // 2)).to("cuda:0")
+    ids = torch.empty_like(pk)
+    wts = torch.empty(pk.shape, dtype=torch.float32, device="cuda:0")
+    measure("packed_decode", 8192, 0, 8, 12 * n,
+            lambda: M.moe_topk_packed_decode(pk, expert_ids=ids, weights=wts), iters_small)
+    del flush_buf
+    torch.cuda.empty_cache()
+    return rows
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the finalize shards by token with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import combine_moe_finalize_amd as M
+    from combine_moe_finalize_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    M.load_library()   # fails loudly when the HIP library is missing
+
+    t0 = time.perf_counter()
+    wl = W.config_workload(4)
+    log(f"generated workload T={wl.T} H={wl.H} k={wl.top_k} P={wl.P} in "
+        f"{time.perf_counter() - t0:.1f} s")
+    kw, _ = upload(wl, torch)
+    T, H, k = wl.T, wl.H, wl.top_k
+    q = torch.empty((T, H), dtype=torch.uint8, device="cuda:0")
+    s = torch.empty((T, H // 128), dtype=torch.uint8, device="cuda:0")
+    nbytes = bytes_quant(T, H, k)
+
+    def step():
+        M.moe_finalize_quant_ue8m0(**kw, out_e4m3=q, scale_e8m0=s)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda:0").fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device-to-device copies")
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kern_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    avg_us = float(np.mean(kern_us))
+    ms_per_step = wall / args.steps * 1e3
+    value = nbytes / (wall / args.steps) / 1e9
+    achieved = nbytes / (avg_us * 1e-6) / 1e9
+    log(f"kernel avg {avg_us:.2f} us (median {np.median(kern_us):.2f}), wall/step "
+        f"{ms_per_step * 1e3:.2f} us, {achieved:.0f} GB/s")
+
+    result = {
+        "metric": "finalize achieved HBM GB/s (% of peak) and us/call at T=1..8192 tokens",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "prefill_finalize_fp8_ue8m0", "tokens": T, "hidden": H,
+                   "experts": wl.E, "top_k": k, "padded_rows": wl.P,
+                   "routed_scaling_factor": wl.rsf, "shared_expert": True,
+                   "routing": "fp32 weights", "io": "bf16 in, e4m3 + ue8m0 out",
+                   "algorithmic_bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counters_traffic(),
+                     "kernel": "finalize_quant_kernel<8,true>",
+                     "kernel_us_avg": round(avg_us, 3),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    del kw, q, s
+    torch.cuda.empty_cache()
+    if not args.no_sweep:
+        result["sweep"] = sweep(torch, M, W)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

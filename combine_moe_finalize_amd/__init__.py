@@ -1,0 +1,18 @@
+"""MI355X (gfx950) deferred MoE finalize.
+
+Python face of libmoe_finalize.so (C ABI in include/moe_finalize.h). The
+four entry points carry the C names; see ``_binding`` for the marshalling
+rules. ``workloads`` draws the seeded synthetic inputs; ``build`` compiles
+the library in-tree.
+"""
+from ._binding import (  # noqa: F401
+    DEVERR_INDEX_OUT_OF_RANGE,
+    MoeFinalizeError,
+    abi_version,
+    load_library,
+    moe_finalize,
+    moe_finalize_quant_ue8m0,
+    moe_finalize_residual_rmsnorm,
+    moe_topk_packed_decode,
+    status_string,
+)

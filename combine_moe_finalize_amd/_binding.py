@@ -1,0 +1,258 @@
+"""ctypes binding of libmoe_finalize.so: argument marshalling only.
+
+Each function checks tensor dtypes, shapes, devices and contiguity, passes
+raw device pointers and the current HIP stream to the C entry point of the
+same name, and raises MoeFinalizeError on a nonzero status. Every step of
+the computation runs in the library's HIP kernels; torch supplies device
+memory and streams. Outputs not supplied are allocated with torch (outside
+graph capture only). There is no fallback: if the library is missing the
+call fails.
+
+Shape rules worth calling out (both are failure modes the pages report):
+  * the index map and weights must be 2-D [T, top_k]; top_k is their last
+    dimension, and a flat tensor is rejected ("[Kimi K2.5] Fuse deferred
+    MoE finalize into next-layer AR + residual + RMSNorm", Key
+    modifications: a flat index caused out-of-bounds reads);
+  * fp32 weights must be float32 and packed words int32; one is never
+    accepted in place of the other ("[Deepseek V4] Keep fp32 routing weights
+    in the mxfp4 trtllm MoE", follow-up commit: fp32 buffers read as bf16
+    broke decoding).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from .build import LIB_PATH
+
+c_void_p = ctypes.c_void_p
+c_i64 = ctypes.c_int64
+c_i32 = ctypes.c_int32
+c_f32 = ctypes.c_float
+
+MOEF_OK = 0
+QUANT_BLOCK = 128
+DEVERR_INDEX_OUT_OF_RANGE = 1
+
+_ROUTED = [c_void_p, c_i64, c_void_p, c_void_p, c_void_p, c_void_p, c_f32]
+_SIGNATURES = {
+    "moe_finalize": _ROUTED + [c_void_p, c_i64, c_i64, c_i32, c_void_p, c_void_p],
+    "moe_finalize_residual_rmsnorm": _ROUTED + [c_void_p, c_void_p, c_f32, c_void_p, c_void_p,
+                                                c_i64, c_i64, c_i32, c_void_p, c_void_p],
+    "moe_finalize_quant_ue8m0": _ROUTED + [c_void_p, c_void_p, c_i64, c_i64, c_i32,
+                                           c_void_p, c_void_p],
+    "moe_topk_packed_decode": [c_void_p, c_i64, c_void_p, c_void_p, c_void_p],
+    "moe_finalize_status_string": [ctypes.c_int],
+    "moe_finalize_abi_version": [],
+}
+
+_lib = None
+
+
+class MoeFinalizeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: status {status}: {status_string(status)}")
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load (once) the built library; raise if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m combine_moe_finalize_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, args in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "moe_finalize_status_string" else ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().moe_finalize_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return load_library().moe_finalize_abi_version()
+
+
+# ------------------------------------------------------------- marshalling
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _tensor(t, name, dtype, shape):
+    """dtype / shape / layout rule of one argument."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _on_device(device, **tensors):
+    """Every given tensor lives on the one GPU device."""
+    if device.type != "cuda":
+        raise ValueError("tensors must be GPU tensors")
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _dev_tensor(t, name, dtype, shape, device):
+    _tensor(t, name, dtype, shape)
+    _on_device(device, **{name: t})
+    return t
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _routed(gemm2_out, idx, topk_weights, topk_packed, shared_out, err_flag):
+    if not isinstance(gemm2_out, torch.Tensor) or gemm2_out.dim() != 2:
+        raise ValueError("gemm2_out must be a 2-D [num_rows, hidden] tensor")
+    if not isinstance(idx, torch.Tensor) or idx.dim() != 2:
+        raise ValueError("expanded_idx_to_permuted_idx must be 2-D [tokens, top_k] "
+                         "(a flat index tensor is rejected)")
+    device = gemm2_out.device
+    P, H = gemm2_out.shape
+    T, K = idx.shape
+    _tensor(gemm2_out, "gemm2_out", torch.bfloat16, (P, H))
+    _tensor(idx, "expanded_idx_to_permuted_idx", torch.int32, (T, K))
+    if (topk_weights is None) == (topk_packed is None):
+        raise ValueError("give exactly one of topk_weights (float32) / topk_packed (int32)")
+    if topk_weights is not None:
+        _tensor(topk_weights, "topk_weights", torch.float32, (T, K))
+    else:
+        _tensor(topk_packed, "topk_packed", torch.int32, (T, K))
+    if shared_out is not None:
+        _tensor(shared_out, "shared_out", torch.bfloat16, (T, H))
+    if err_flag is not None:
+        _tensor(err_flag, "err_flag", torch.int32, (1,))
+    _on_device(device, gemm2_out=gemm2_out, expanded_idx_to_permuted_idx=idx,
+               topk_weights=topk_weights, topk_packed=topk_packed, shared_out=shared_out,
+               err_flag=err_flag)
+    args = [_ptr(gemm2_out), P, _ptr(idx), _ptr(topk_weights), _ptr(topk_packed),
+            _ptr(shared_out)]
+    return device, T, H, K, args
+
+
+def _check(fn, status):
+    if status != MOEF_OK:
+        raise MoeFinalizeError(fn, status)
+
+
+# ------------------------------------------------------------- entry points
+
+def moe_finalize(gemm2_out: torch.Tensor, expanded_idx_to_permuted_idx: torch.Tensor, *,
+                 topk_weights: Optional[torch.Tensor] = None,
+                 topk_packed: Optional[torch.Tensor] = None,
+                 shared_out: Optional[torch.Tensor] = None,
+                 routed_scaling_factor: float = 1.0,
+                 out: Optional[torch.Tensor] = None,
+                 err_flag: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [T, H] deferred finalize (see moe_finalize in moe_finalize.h)."""
+    device, T, H, K, args = _routed(gemm2_out, expanded_idx_to_permuted_idx, topk_weights,
+                                    topk_packed, shared_out, err_flag)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    _dev_tensor(out, "out", torch.bfloat16, (T, H), device)
+    st = load_library().moe_finalize(*args, float(routed_scaling_factor), _ptr(out), T, H, K,
+                                     _ptr(err_flag), _stream(device))
+    _check("moe_finalize", st)
+    return out
+
+
+def moe_finalize_residual_rmsnorm(gemm2_out: torch.Tensor,
+                                  expanded_idx_to_permuted_idx: torch.Tensor, *,
+                                  residual: torch.Tensor, gamma: torch.Tensor,
+                                  eps: float = 1e-6,
+                                  topk_weights: Optional[torch.Tensor] = None,
+                                  topk_packed: Optional[torch.Tensor] = None,
+                                  shared_out: Optional[torch.Tensor] = None,
+                                  routed_scaling_factor: float = 1.0,
+                                  residual_out: Optional[torch.Tensor] = None,
+                                  normed: Optional[torch.Tensor] = None,
+                                  err_flag: Optional[torch.Tensor] = None):
+    """(residual_out, normed), both bf16 [T, H]. residual_out may be residual
+    (in-place update)."""
+    device, T, H, K, args = _routed(gemm2_out, expanded_idx_to_permuted_idx, topk_weights,
+                                    topk_packed, shared_out, err_flag)
+    _dev_tensor(residual, "residual", torch.bfloat16, (T, H), device)
+    _dev_tensor(gamma, "gamma", torch.bfloat16, (H,), device)
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    if normed is None:
+        normed = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    _dev_tensor(residual_out, "residual_out", torch.bfloat16, (T, H), device)
+    _dev_tensor(normed, "normed", torch.bfloat16, (T, H), device)
+    st = load_library().moe_finalize_residual_rmsnorm(
+        *args, float(routed_scaling_factor), _ptr(residual), _ptr(gamma), float(eps),
+        _ptr(residual_out), _ptr(normed), T, H, K, _ptr(err_flag), _stream(device))
+    _check("moe_finalize_residual_rmsnorm", st)
+    return residual_out, normed
+
+
+def moe_finalize_quant_ue8m0(gemm2_out: torch.Tensor,
+                             expanded_idx_to_permuted_idx: torch.Tensor, *,
+                             topk_weights: Optional[torch.Tensor] = None,
+                             topk_packed: Optional[torch.Tensor] = None,
+                             shared_out: Optional[torch.Tensor] = None,
+                             routed_scaling_factor: float = 1.0,
+                             out_e4m3: Optional[torch.Tensor] = None,
+                             scale_e8m0: Optional[torch.Tensor] = None,
+                             err_flag: Optional[torch.Tensor] = None):
+    """(codes uint8 [T, H] as OCP E4M3 bits, scale bytes uint8 [T, H/128])."""
+    device, T, H, K, args = _routed(gemm2_out, expanded_idx_to_permuted_idx, topk_weights,
+                                    topk_packed, shared_out, err_flag)
+    if H % QUANT_BLOCK:
+        raise ValueError("hidden must be a multiple of 128 for the UE8M0 epilogue")
+    if out_e4m3 is None:
+        out_e4m3 = torch.empty((T, H), dtype=torch.uint8, device=device)
+    if scale_e8m0 is None:
+        scale_e8m0 = torch.empty((T, H // QUANT_BLOCK), dtype=torch.uint8, device=device)
+    if out_e4m3.dtype == torch.float8_e4m3fn:
+        out_e4m3 = out_e4m3.view(torch.uint8)
+    _dev_tensor(out_e4m3, "out_e4m3", torch.uint8, (T, H), device)
+    _dev_tensor(scale_e8m0, "scale_e8m0", torch.uint8, (T, H // QUANT_BLOCK), device)
+    st = load_library().moe_finalize_quant_ue8m0(
+        *args, float(routed_scaling_factor), _ptr(out_e4m3), _ptr(scale_e8m0), T, H, K,
+        _ptr(err_flag), _stream(device))
+    _check("moe_finalize_quant_ue8m0", st)
+    return out_e4m3, scale_e8m0
+
+
+def moe_topk_packed_decode(topk_packed: torch.Tensor, *,
+                           expert_ids: Optional[torch.Tensor] = None,
+                           weights: Optional[torch.Tensor] = None):
+    """(expert_ids int32, weights float32), both shaped like topk_packed."""
+    if not isinstance(topk_packed, torch.Tensor):
+        raise TypeError("topk_packed must be a torch.Tensor")
+    device = topk_packed.device
+    shape = tuple(topk_packed.shape)
+    _dev_tensor(topk_packed, "topk_packed", torch.int32, shape, device)
+    if expert_ids is None:
+        expert_ids = torch.empty(shape, dtype=torch.int32, device=device)
+    if weights is None:
+        weights = torch.empty(shape, dtype=torch.float32, device=device)
+    _dev_tensor(expert_ids, "expert_ids", torch.int32, shape, device)
+    _dev_tensor(weights, "weights", torch.float32, shape, device)
+    st = load_library().moe_topk_packed_decode(_ptr(topk_packed), topk_packed.numel(),
+                                               _ptr(expert_ids), _ptr(weights),
+                                               _stream(device))
+    _check("moe_topk_packed_decode", st)
+    return expert_ids, weights

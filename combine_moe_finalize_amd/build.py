@@ -1,0 +1,62 @@
+"""Build the gfx950 shared library libmoe_finalize.so in-tree with hipcc.
+
+    python -m combine_moe_finalize_amd.build
+
+Flags: fp-contract off (the finalize's fp32 operation order is part of its
+contract: a separate multiply and add per gathered row, no fused
+multiply-add), packed-fp32 instructions disabled, -O3, gfx950 only.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_DIR = os.path.join(PKG, "_lib")
+LIB_NAME = "libmoe_finalize.so"
+LIB_PATH = os.path.join(LIB_DIR, LIB_NAME)
+
+SOURCES = ["moef_api.hip", "finalize_kernels.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(p):
+        raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+    return p
+
+
+def compile_command(out: str) -> list:
+    return [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}",
+            "-fPIC", "-shared", "-ffp-contract=off",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-function",
+            "-I", INCLUDE, "-I", CSRC,
+            *[os.path.join(CSRC, s) for s in SOURCES],
+            "-o", out]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (always, even if one is present). Returns its path."""
+    os.makedirs(LIB_DIR, exist_ok=True)
+    tmp = LIB_PATH + ".tmp"
+    cmd = compile_command(tmp)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
+    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs, file=sys.stderr)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

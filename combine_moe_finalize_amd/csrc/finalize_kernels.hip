@@ -1,0 +1,451 @@
+// gfx950 kernels of the deferred MoE finalize.
+//
+// What they compute ("Support deferred MoE finalize for MXFP4 and FP8
+// block-scale", Motivation and Modifications item 2; "[Kimi K2.5] Fuse
+// deferred MoE finalize into next-layer AR + residual + RMSNorm", Key
+// modifications and "Numerics & speed"): for every token t and column h,
+//   acc = +0;  for k ascending: acc = acc + w'[t,k] * x[perm[t,k], h]
+//   acc = acc + shared[t,h];  [acc = acc + residual[t,h]]
+// with w' = fp32(w * routed_scaling_factor), every operation rounded to fp32
+// (this file is built with fp-contract off: no fused multiply-add), then one
+// round-to-nearest-even to bf16.
+//
+// Work decomposition. The path is a gather-reduce bound by HBM bandwidth, not
+// a contraction, so there is no MFMA here. One wavefront owns one
+// (token, 512-column chunk): each of its 64 lanes owns 8 consecutive bf16
+// columns and moves them with one 16-byte load per gathered row. The token's
+// top_k indices and weights are wave-uniform and land in scalar registers;
+// the weight (times the routed scaling factor) stays in a register for the
+// whole chunk. All top_k row loads and the shared / residual loads are issued
+// before the first add, so a lane has (top_k + 2) x 16 bytes in flight.
+// Gathered rows are read exactly once, so they use non-temporal loads.
+//
+// Epilogues:
+//  * RMSNorm: one workgroup per token (up to 16 waves), the row stays in
+//    registers; sum of squares by cross-lane shuffles in the wave, then LDS
+//    across waves, summed in a fixed order so every lane sees the same value.
+//  * UE8M0 quant: a 1 x 128 block is 16 lanes x 8 columns, one DPP row; its
+//    absolute maximum takes four DPP row rotations, the power-of-two exponent
+//    comes from the maximum's bit fields, and each value is scaled exactly by
+//    ldexp and rounded to OCP E4M3 in integer arithmetic.
+//    ("[FP8][MoE] Honor UE8M0 activation scales in Triton MoE", Motivation
+//    and "More context".)
+
+#include "moef_internal.h"
+
+namespace moef {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Kernel-side view of one routed call.
+struct GatherArgs {
+  const u32x4* g2;        // gemm2_out as 16-byte vectors, row stride h8
+  int64_t num_rows;
+  const int32_t* idx;     // [T, k]
+  const uint32_t* w;      // [T, k] fp32 bits or packed words
+  const u32x4* shared;    // [T, h8] or nullptr
+  float rsf;
+  int32_t packed;
+  int32_t tokens;
+  int32_t h8;             // hidden / 8
+  int32_t k;
+  int32_t nchunks;        // ceil(h8 / 64)
+  int32_t* err;
+};
+
+// ------------------------------------------------------------ bf16 helpers
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> quiet NaN keeping the sign.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void unpack8(const u32x4 v, float x[8]) {
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+  x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+  x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ u32x4 pack8_bits(const uint32_t b[8]) {
+  u32x4 v;
+  v.x = b[0] | (b[1] << 16);
+  v.y = b[2] | (b[3] << 16);
+  v.z = b[4] | (b[5] << 16);
+  v.w = b[6] | (b[7] << 16);
+  return v;
+}
+
+// ------------------------------------------------------------- gather core
+
+// Loads the token's routing: gathered row (or -1 when the slot is skipped)
+// and w' = fp32(w * rsf). Reads are wave-uniform (scalar loads).
+template <int KMAX, bool EXACT>
+__device__ __forceinline__ void load_route(const GatherArgs& a, int t,
+                                           int32_t row[KMAX], float w[KMAX]) {
+  const int64_t base = (int64_t)t * a.k;
+  uint32_t word[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    row[j] = -1;
+    word[j] = 0u;
+    if (EXACT || j < a.k) {
+      row[j] = a.idx[base + j];
+      word[j] = a.w[base + j];
+    }
+  }
+  bool oob = false;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    w[j] = __uint_as_float(a.packed ? (word[j] << 16) : word[j]) * a.rsf;
+    if ((int64_t)row[j] >= a.num_rows) {   // out of range: skip and report
+      oob = true;
+      row[j] = -1;
+    }                                      // negative: expert not local, skip
+  }
+  if (oob && a.err != nullptr && (threadIdx.x & 63) == 0)
+    atomicOr(a.err, MOEF_DEVERR_INDEX_OUT_OF_RANGE);
+}
+
+// acc[0..7] for columns [8*col, 8*col + 8) of token t: the weighted sum of the
+// gathered rows, then + shared, then + residual (when given), each in fp32.
+template <int KMAX, bool EXACT>
+__device__ __forceinline__ void finalize_acc(const GatherArgs& a, int t, int64_t col,
+                                             const int32_t row[KMAX], const float w[KMAX],
+                                             const u32x4* residual_row, float acc[8]) {
+  u32x4 v[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if ((EXACT || j < a.k) && row[j] >= 0)
+      v[j] = __builtin_nontemporal_load(a.g2 + (int64_t)row[j] * a.h8 + col);
+  }
+  u32x4 s = {0u, 0u, 0u, 0u};
+  u32x4 r = {0u, 0u, 0u, 0u};
+  if (a.shared != nullptr) s = __builtin_nontemporal_load(a.shared + (int64_t)t * a.h8 + col);
+  if (residual_row != nullptr) r = residual_row[col];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if ((EXACT || j < a.k) && row[j] >= 0) {
+      float x[8];
+      unpack8(v[j], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + w[j] * x[e];
+    }
+  }
+  if (a.shared != nullptr) {
+    float x[8];
+    unpack8(s, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + x[e];
+  }
+  if (residual_row != nullptr) {
+    float x[8];
+    unpack8(r, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + x[e];
+  }
+}
+
+// ------------------------------------------------------------------ plain
+
+template <int KMAX, bool EXACT>
+__global__ void __launch_bounds__(kWavesPerBlock * kWaveLanes)
+finalize_kernel(GatherArgs a, u32x4* __restrict__ out) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int unit = (int)blockIdx.x * kWavesPerBlock + wave;
+  if ((int64_t)unit >= (int64_t)a.tokens * a.nchunks) return;   // whole waves
+  const int t = unit / a.nchunks;
+  const int colv = (unit - t * a.nchunks) * kWaveLanes + lane;
+  const bool active = colv < a.h8;
+  const int64_t col = active ? colv : a.h8 - 1;   // keep every lane's loads in bounds
+
+  int32_t row[KMAX];
+  float w[KMAX];
+  load_route<KMAX, EXACT>(a, t, row, w);
+  float acc[8];
+  finalize_acc<KMAX, EXACT>(a, t, col, row, w, nullptr, acc);
+
+  uint32_t b[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = bf16_rne(acc[e]);
+  if (active) out[(int64_t)t * a.h8 + colv] = pack8_bits(b);
+}
+
+// ------------------------------------------------------- residual + RMSNorm
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+template <int KMAX, bool EXACT, int CPT>
+__global__ void __launch_bounds__(kNormMaxThreads)
+finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __restrict__ gamma,
+                        float eps, float inv_hidden, u32x4* residual_out,
+                        u32x4* __restrict__ normed) {
+  __shared__ float partial[kNormMaxThreads / kWaveLanes];
+  const int t = blockIdx.x;
+  const int nthreads = blockDim.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+
+  int32_t row[KMAX];
+  float w[KMAX];
+  load_route<KMAX, EXACT>(a, t, row, w);
+  const u32x4* res_row = residual + (int64_t)t * a.h8;
+
+  float ro[CPT][8];
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int colv = threadIdx.x + i * nthreads;
+    const bool active = colv < a.h8;
+    const int64_t col = active ? colv : a.h8 - 1;
+    float acc[8];
+    finalize_acc<KMAX, EXACT>(a, t, col, row, w, res_row, acc);
+    uint32_t b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      b[e] = bf16_rne(acc[e]);
+      ro[i][e] = __uint_as_float(b[e] << 16);
+    }
+    if (active) {
+      residual_out[(int64_t)t * a.h8 + colv] = pack8_bits(b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = ss + ro[i][e] * ro[i][e];
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) partial[wave] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+  const int nw = nthreads >> 6;
+  for (int i = 0; i < nw; ++i) tot = tot + partial[i];
+  const float inv = rsqrtf(tot * inv_hidden + eps);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int colv = threadIdx.x + i * nthreads;
+    if (colv < a.h8) {
+      float g[8];
+      unpack8(gamma[colv], g);
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = bf16_rne((ro[i][e] * inv) * g[e]);
+      normed[(int64_t)t * a.h8 + colv] = pack8_bits(b);
+    }
+  }
+}
+
+// ------------------------------------------------------- UE8M0 / E4M3 quant
+
+// Largest value across the 16 lanes of a DPP row (every lane gets it).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xF, 0xF, false)));
+  return v;
+}
+
+// Least e with amax <= 448 * 2^e, clamped to [-127, 127]. With
+// amax = 2^E * 1.f and 448 = 2^8 * 1.75: e = E - 8, plus one when 1.f > 1.75
+// (fraction field above 0x600000). Zero and subnormal amax clamp to -127
+// (every subnormal is below 448 * 2^-127); inf / NaN give 127.
+__device__ __forceinline__ int ue8m0_exponent(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int ef = (int)(b >> 23);
+  if (ef == 0) return -127;
+  if (ef >= 255) return 127;
+  const int e = ef - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : e;
+}
+
+// OCP E4M3 ("e4m3fn": bias 7, max 448, NaN S.1111.111) code of s, nearest
+// even, subnormals kept, sign of zero kept. Magnitudes rounding above 448 and
+// NaN give the NaN code.
+__device__ __forceinline__ uint32_t e4m3_rne(float s) {
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x3C800000u) {                               // |s| >= 2^-6: normal
+    a = (a + 0x7FFFFu + ((a >> 20) & 1u)) & 0xFFF00000u; // 3 fraction bits, ties even
+    code = (a > 0x43E00000u) ? 0x7Fu                     // beyond 448 (or inf / NaN)
+                             : ((((a >> 23) - 120u) << 3) | ((a >> 20) & 7u));
+  } else {                                              // subnormal: multiples of 2^-9
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);   // 0..8, exact scaling
+  }
+  return code | sign;
+}
+
+template <int KMAX, bool EXACT>
+__global__ void __launch_bounds__(kWavesPerBlock * kWaveLanes)
+finalize_quant_kernel(GatherArgs a, u32x2* __restrict__ out_q, uint8_t* __restrict__ scale) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int unit = (int)blockIdx.x * kWavesPerBlock + wave;
+  if ((int64_t)unit >= (int64_t)a.tokens * a.nchunks) return;   // whole waves
+  const int t = unit / a.nchunks;
+  const int colv = (unit - t * a.nchunks) * kWaveLanes + lane;
+  const bool active = colv < a.h8;       // h8 % 16 == 0: whole DPP rows agree
+  const int64_t col = active ? colv : a.h8 - 1;
+
+  int32_t row[KMAX];
+  float w[KMAX];
+  load_route<KMAX, EXACT>(a, t, row, w);
+  float acc[8];
+  finalize_acc<KMAX, EXACT>(a, t, col, row, w, nullptr, acc);
+
+  float y[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    y[e] = __uint_as_float(bf16_rne(acc[e]) << 16);   // the bf16 finalize result
+    amax = fmaxf(amax, fabsf(y[e]));
+  }
+  if (!active) amax = 0.0f;
+  amax = row16_max(amax);
+  const int ex = ue8m0_exponent(amax);
+  u32x2 q = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    q.x |= e4m3_rne(ldexpf(y[e], -ex)) << (8 * e);
+    q.y |= e4m3_rne(ldexpf(y[e + 4], -ex)) << (8 * e);
+  }
+  if (active) {
+    out_q[(int64_t)t * a.h8 + colv] = q;
+    if ((lane & 15) == 0) scale[(int64_t)t * (a.h8 >> 4) + (colv >> 4)] = (uint8_t)(ex + 127);
+  }
+}
+
+// ------------------------------------------------------------ packed decode
+
+// (expert_id << 16) | bf16(weight) -> id (logical shift) and exact fp32 weight.
+// ("[Deepseek V4] Keep fp32 routing weights in the mxfp4 trtllm MoE", PR
+// description.)
+__global__ void __launch_bounds__(256)
+packed_decode_kernel(const uint32_t* __restrict__ packed, int64_t n,
+                     int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t word = packed[i];
+  if (ids != nullptr) ids[i] = (int32_t)(word >> 16);
+  if (w != nullptr) w[i] = __uint_as_float(word << 16);
+}
+
+// ---------------------------------------------------------------- dispatch
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Exact instantiations for the common top_k, guarded ones otherwise.
+template <typename F>
+hipError_t dispatch_top_k(int k, F&& f) {
+  switch (k) {
+    case 1: return f(IC<1>{}, std::true_type{});
+    case 2: return f(IC<2>{}, std::true_type{});
+    case 4: return f(IC<4>{}, std::true_type{});
+    case 6: return f(IC<6>{}, std::true_type{});
+    case 8: return f(IC<8>{}, std::true_type{});
+    default:
+      if (k <= 4) return f(IC<4>{}, std::false_type{});
+      if (k <= 8) return f(IC<8>{}, std::false_type{});
+      return f(IC<16>{}, std::false_type{});
+  }
+}
+
+GatherArgs make_args(const Routed& r) {
+  GatherArgs a;
+  a.g2 = reinterpret_cast<const u32x4*>(r.gemm2_out);
+  a.num_rows = r.num_rows;
+  a.idx = r.idx;
+  a.w = r.weights;
+  a.shared = reinterpret_cast<const u32x4*>(r.shared);
+  a.rsf = r.rsf;
+  a.packed = r.packed ? 1 : 0;
+  a.tokens = (int32_t)r.tokens;
+  a.h8 = (int32_t)(r.hidden / kVecElems);
+  a.k = r.top_k;
+  a.nchunks = (a.h8 + kWaveLanes - 1) / kWaveLanes;
+  a.err = r.err_flag;
+  return a;
+}
+
+unsigned int plain_blocks(const GatherArgs& a) {
+  const int64_t units = (int64_t)a.tokens * a.nchunks;
+  return (unsigned int)((units + kWavesPerBlock - 1) / kWavesPerBlock);
+}
+
+}  // namespace
+
+hipError_t launch_finalize(const Routed& r, uint16_t* out, hipStream_t stream) {
+  const GatherArgs a = make_args(r);
+  u32x4* o = reinterpret_cast<u32x4*>(out);
+  return dispatch_top_k(a.k, [&](auto km, auto ex) {
+    constexpr int KM = decltype(km)::value;
+    constexpr bool EX = decltype(ex)::value;
+    hipLaunchKernelGGL((finalize_kernel<KM, EX>), dim3(plain_blocks(a)),
+                       dim3(kWavesPerBlock * kWaveLanes), 0, stream, a, o);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_finalize_rmsnorm(const Routed& r, const uint16_t* residual,
+                                   const uint16_t* gamma, float eps,
+                                   uint16_t* residual_out, uint16_t* normed,
+                                   hipStream_t stream) {
+  const GatherArgs a = make_args(r);
+  int threads = ((a.h8 + kWaveLanes - 1) / kWaveLanes) * kWaveLanes;
+  if (threads > kNormMaxThreads) threads = kNormMaxThreads;
+  const int cpt = (a.h8 + threads - 1) / threads;   // 1 or 2 (hidden <= 16384)
+  const float inv_hidden = 1.0f / (float)r.hidden;
+  const u32x4* res = reinterpret_cast<const u32x4*>(residual);
+  const u32x4* gam = reinterpret_cast<const u32x4*>(gamma);
+  u32x4* ro = reinterpret_cast<u32x4*>(residual_out);
+  u32x4* nm = reinterpret_cast<u32x4*>(normed);
+  return dispatch_top_k(a.k, [&](auto km, auto ex) {
+    constexpr int KM = decltype(km)::value;
+    constexpr bool EX = decltype(ex)::value;
+    if (cpt == 1)
+      hipLaunchKernelGGL((finalize_rmsnorm_kernel<KM, EX, 1>), dim3(a.tokens), dim3(threads),
+                         0, stream, a, res, gam, eps, inv_hidden, ro, nm);
+    else
+      hipLaunchKernelGGL((finalize_rmsnorm_kernel<KM, EX, 2>), dim3(a.tokens), dim3(threads),
+                         0, stream, a, res, gam, eps, inv_hidden, ro, nm);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_finalize_quant(const Routed& r, uint8_t* out_e4m3, uint8_t* scale_e8m0,
+                                 hipStream_t stream) {
+  const GatherArgs a = make_args(r);
+  u32x2* q = reinterpret_cast<u32x2*>(out_e4m3);
+  return dispatch_top_k(a.k, [&](auto km, auto ex) {
+    constexpr int KM = decltype(km)::value;
+    constexpr bool EX = decltype(ex)::value;
+    hipLaunchKernelGGL((finalize_quant_kernel<KM, EX>), dim3(plain_blocks(a)),
+                       dim3(kWavesPerBlock * kWaveLanes), 0, stream, a, q, scale_e8m0);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_packed_decode(const int32_t* packed, int64_t n, int32_t* expert_ids,
+                                float* weights, hipStream_t stream) {
+  const unsigned int blocks = (unsigned int)((n + 255) / 256);
+  hipLaunchKernelGGL(packed_decode_kernel, dim3(blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const uint32_t*>(packed), n, expert_ids, weights);
+  return hipGetLastError();
+}
+
+}  // namespace moef

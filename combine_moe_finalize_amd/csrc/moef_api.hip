@@ -1,0 +1,228 @@
+// C-ABI entry points of the deferred MoE finalize library.
+//
+// Each entry point validates every argument before it makes any HIP runtime
+// call (so a rejected call enqueues nothing and the checks run on a machine
+// without a GPU), then launches on the caller's stream and returns without
+// synchronizing. The library allocates nothing and keeps no state, so a call
+// can be captured into a HIP graph (the pages size their workspaces before
+// graph capture and never grow them inside: "[Kimi K2.5] Fuse deferred MoE
+// finalize into next-layer AR + residual + RMSNorm", Key modifications).
+
+#include <type_traits>
+
+#include "moef_internal.h"
+
+namespace {
+
+using moef::Routed;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte ranges [p, p + n) overlap?
+bool overlap(const void* p, int64_t np, const void* q, int64_t nq) {
+  if (p == nullptr || q == nullptr || np <= 0 || nq <= 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uintptr_t b = reinterpret_cast<uintptr_t>(q);
+  return a < b + (uintptr_t)nq && b < a + (uintptr_t)np;
+}
+
+struct Span {
+  const void* p;
+  int64_t bytes;
+};
+
+// Shape rules shared by the finalize entry points. Sets *noop for T == 0.
+int check_shape(int64_t num_rows, int64_t tokens, int64_t hidden, int32_t top_k, bool* noop) {
+  *noop = false;
+  if (tokens < 0 || num_rows < 0) return MOEF_ERR_BAD_SHAPE;
+  if (top_k < 1 || top_k > MOEF_MAX_TOP_K) return MOEF_ERR_BAD_SHAPE;
+  if (hidden < 1) return MOEF_ERR_BAD_SHAPE;
+  if (hidden % moef::kVecElems != 0 || hidden > MOEF_MAX_HIDDEN) return MOEF_ERR_UNSUPPORTED;
+  if (num_rows > INT32_MAX) return MOEF_ERR_UNSUPPORTED;   // rows are named by int32
+  if (tokens > INT32_MAX) return MOEF_ERR_UNSUPPORTED;
+  const int64_t nchunks = (hidden / moef::kVecElems + moef::kWaveLanes - 1) / moef::kWaveLanes;
+  if (tokens * nchunks > moef::kMaxUnits) return MOEF_ERR_UNSUPPORTED;
+  if (tokens == 0) *noop = true;
+  return MOEF_OK;
+}
+
+// Pointer, format and alignment rules of the routed inputs.
+int check_routed_inputs(const Routed& r) {
+  if (r.idx == nullptr || r.weights == nullptr) {
+    return r.idx == nullptr ? MOEF_ERR_NULL_POINTER : MOEF_ERR_BAD_FORMAT;
+  }
+  if (r.num_rows > 0 && r.gemm2_out == nullptr) return MOEF_ERR_NULL_POINTER;
+  if (!aligned(r.gemm2_out, 16) || !aligned(r.shared, 16)) return MOEF_ERR_MISALIGNED;
+  if (!aligned(r.idx, 4) || !aligned(r.weights, 4) || !aligned(r.err_flag, 4))
+    return MOEF_ERR_MISALIGNED;
+  return MOEF_OK;
+}
+
+// Fills the routed block; exactly one weight format must be given.
+int make_routed(Routed* r, const uint16_t* gemm2_out, int64_t num_rows, const int32_t* idx,
+                const float* w32, const int32_t* packed, const uint16_t* shared, float rsf,
+                int64_t tokens, int64_t hidden, int32_t top_k, int32_t* err_flag) {
+  if ((w32 == nullptr) == (packed == nullptr)) return MOEF_ERR_BAD_FORMAT;
+  r->gemm2_out = gemm2_out;
+  r->num_rows = num_rows;
+  r->idx = idx;
+  r->weights = w32 != nullptr ? reinterpret_cast<const uint32_t*>(w32)
+                              : reinterpret_cast<const uint32_t*>(packed);
+  r->packed = packed != nullptr;
+  r->shared = shared;
+  r->rsf = rsf;
+  r->tokens = tokens;
+  r->hidden = hidden;
+  r->top_k = top_k;
+  r->err_flag = err_flag;
+  return MOEF_OK;
+}
+
+// The input byte ranges of a routed call (for alias checks).
+int routed_spans(const Routed& r, Span* s) {
+  const int64_t row_bytes = r.hidden * 2;
+  const int64_t slot_bytes = r.tokens * r.top_k * 4;
+  s[0] = {r.gemm2_out, r.num_rows * row_bytes};
+  s[1] = {r.idx, slot_bytes};
+  s[2] = {r.weights, slot_bytes};
+  s[3] = {r.shared, r.shared ? r.tokens * row_bytes : 0};
+  s[4] = {r.err_flag, r.err_flag ? 4 : 0};
+  return 5;
+}
+
+bool overlaps_any(const void* p, int64_t n, const Span* s, int ns) {
+  for (int i = 0; i < ns; ++i)
+    if (overlap(p, n, s[i].p, s[i].bytes)) return true;
+  return false;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOEF_OK : MOEF_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_finalize_abi_version(void) { return MOEF_ABI_VERSION; }
+
+const char* moe_finalize_status_string(int status) {
+  switch (status) {
+    case MOEF_OK: return "ok";
+    case MOEF_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case MOEF_ERR_BAD_SHAPE: return "bad shape (negative count, hidden or top_k out of range)";
+    case MOEF_ERR_UNSUPPORTED: return "unsupported size (hidden alignment or limits)";
+    case MOEF_ERR_MISALIGNED: return "pointer misaligned";
+    case MOEF_ERR_BAD_FORMAT: return "give exactly one routing-weight format (fp32 or packed)";
+    case MOEF_ERR_BAD_ALIAS: return "an output overlaps an input or another output";
+    case MOEF_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_finalize(const uint16_t* gemm2_out, int64_t num_rows,
+                 const int32_t* expanded_idx_to_permuted_idx, const float* topk_weights,
+                 const int32_t* topk_packed, const uint16_t* shared_out,
+                 float routed_scaling_factor, uint16_t* out, int64_t num_tokens,
+                 int64_t hidden, int32_t top_k, int32_t* err_flag, void* stream) {
+  bool noop;
+  int st = check_shape(num_rows, num_tokens, hidden, top_k, &noop);
+  if (st != MOEF_OK || noop) return st;
+  Routed r;
+  st = make_routed(&r, gemm2_out, num_rows, expanded_idx_to_permuted_idx, topk_weights,
+                   topk_packed, shared_out, routed_scaling_factor, num_tokens, hidden,
+                   top_k, err_flag);
+  if (st != MOEF_OK) return st;
+  if ((st = check_routed_inputs(r)) != MOEF_OK) return st;
+  if (out == nullptr) return MOEF_ERR_NULL_POINTER;
+  if (!aligned(out, 16)) return MOEF_ERR_MISALIGNED;
+  Span s[8];
+  const int ns = routed_spans(r, s);
+  if (overlaps_any(out, num_tokens * hidden * 2, s, ns)) return MOEF_ERR_BAD_ALIAS;
+  return hip_status(moef::launch_finalize(r, out, static_cast<hipStream_t>(stream)));
+}
+
+int moe_finalize_residual_rmsnorm(const uint16_t* gemm2_out, int64_t num_rows,
+                                  const int32_t* expanded_idx_to_permuted_idx,
+                                  const float* topk_weights, const int32_t* topk_packed,
+                                  const uint16_t* shared_out, float routed_scaling_factor,
+                                  const uint16_t* residual, const uint16_t* gamma, float eps,
+                                  uint16_t* residual_out, uint16_t* normed,
+                                  int64_t num_tokens, int64_t hidden, int32_t top_k,
+                                  int32_t* err_flag, void* stream) {
+  bool noop;
+  int st = check_shape(num_rows, num_tokens, hidden, top_k, &noop);
+  if (st != MOEF_OK) return st;
+  if (hidden > MOEF_MAX_HIDDEN_RMSNORM) return MOEF_ERR_UNSUPPORTED;
+  if (noop) return MOEF_OK;
+  Routed r;
+  st = make_routed(&r, gemm2_out, num_rows, expanded_idx_to_permuted_idx, topk_weights,
+                   topk_packed, shared_out, routed_scaling_factor, num_tokens, hidden,
+                   top_k, err_flag);
+  if (st != MOEF_OK) return st;
+  if ((st = check_routed_inputs(r)) != MOEF_OK) return st;
+  if (residual == nullptr || gamma == nullptr || residual_out == nullptr || normed == nullptr)
+    return MOEF_ERR_NULL_POINTER;
+  if (!aligned(residual, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) ||
+      !aligned(normed, 16))
+    return MOEF_ERR_MISALIGNED;
+  const int64_t tb = num_tokens * hidden * 2;
+  Span s[8];
+  int ns = routed_spans(r, s);
+  s[ns++] = {gamma, hidden * 2};
+  // residual_out may be residual itself, but no other overlap is allowed
+  if (overlaps_any(residual_out, tb, s, ns)) return MOEF_ERR_BAD_ALIAS;
+  if (residual_out != residual && overlap(residual_out, tb, residual, tb)) return MOEF_ERR_BAD_ALIAS;
+  s[ns++] = {residual, tb};
+  if (overlaps_any(normed, tb, s, ns) || overlap(normed, tb, residual_out, tb))
+    return MOEF_ERR_BAD_ALIAS;
+  return hip_status(moef::launch_finalize_rmsnorm(r, residual, gamma, eps, residual_out, normed,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int moe_finalize_quant_ue8m0(const uint16_t* gemm2_out, int64_t num_rows,
+                             const int32_t* expanded_idx_to_permuted_idx,
+                             const float* topk_weights, const int32_t* topk_packed,
+                             const uint16_t* shared_out, float routed_scaling_factor,
+                             uint8_t* out_e4m3, uint8_t* scale_e8m0, int64_t num_tokens,
+                             int64_t hidden, int32_t top_k, int32_t* err_flag, void* stream) {
+  bool noop;
+  int st = check_shape(num_rows, num_tokens, hidden, top_k, &noop);
+  if (st != MOEF_OK) return st;
+  if (hidden % MOEF_QUANT_BLOCK != 0) return MOEF_ERR_UNSUPPORTED;
+  if (noop) return MOEF_OK;
+  Routed r;
+  st = make_routed(&r, gemm2_out, num_rows, expanded_idx_to_permuted_idx, topk_weights,
+                   topk_packed, shared_out, routed_scaling_factor, num_tokens, hidden,
+                   top_k, err_flag);
+  if (st != MOEF_OK) return st;
+  if ((st = check_routed_inputs(r)) != MOEF_OK) return st;
+  if (out_e4m3 == nullptr || scale_e8m0 == nullptr) return MOEF_ERR_NULL_POINTER;
+  if (!aligned(out_e4m3, 8)) return MOEF_ERR_MISALIGNED;
+  const int64_t qb = num_tokens * hidden;
+  const int64_t sb = num_tokens * (hidden / MOEF_QUANT_BLOCK);
+  Span s[8];
+  const int ns = routed_spans(r, s);
+  if (overlaps_any(out_e4m3, qb, s, ns) || overlaps_any(scale_e8m0, sb, s, ns) ||
+      overlap(out_e4m3, qb, scale_e8m0, sb))
+    return MOEF_ERR_BAD_ALIAS;
+  return hip_status(moef::launch_finalize_quant(r, out_e4m3, scale_e8m0,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int moe_topk_packed_decode(const int32_t* packed, int64_t n, int32_t* expert_ids,
+                           float* weights, void* stream) {
+  if (n < 0) return MOEF_ERR_BAD_SHAPE;
+  if (n > moef::kMaxUnits * 256) return MOEF_ERR_UNSUPPORTED;
+  if (n == 0) return MOEF_OK;
+  if (packed == nullptr || (expert_ids == nullptr && weights == nullptr))
+    return MOEF_ERR_NULL_POINTER;
+  if (!aligned(packed, 4) || !aligned(expert_ids, 4) || !aligned(weights, 4))
+    return MOEF_ERR_MISALIGNED;
+  const int64_t nb = n * 4;
+  if (overlap(expert_ids, nb, packed, nb) || overlap(weights, nb, packed, nb) ||
+      overlap(expert_ids, nb, weights, nb))
+    return MOEF_ERR_BAD_ALIAS;
+  return hip_status(moef::launch_packed_decode(packed, n, expert_ids, weights,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

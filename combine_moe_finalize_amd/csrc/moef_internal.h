@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI entry points (moef_api.hip) and the
+// gfx950 kernels (finalize_kernels.hip). Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_finalize.h"
+
+namespace moef {
+
+// The routed half of every finalize call: gemm2_out rows, the [T, top_k]
+// index map and weights, the optional shared-expert output and the routed
+// scaling factor. Validated by the entry points before any launch.
+struct Routed {
+  const uint16_t* gemm2_out;  // bf16 [num_rows, hidden]
+  int64_t num_rows;
+  const int32_t* idx;         // int32 [T, top_k]
+  const uint32_t* weights;    // fp32 bits or packed words [T, top_k]
+  bool packed;                // true: (id << 16) | bf16 bits
+  const uint16_t* shared;     // bf16 [T, hidden] or nullptr
+  float rsf;
+  int64_t tokens;
+  int64_t hidden;
+  int32_t top_k;
+  int32_t* err_flag;          // optional device int32
+};
+
+hipError_t launch_finalize(const Routed& r, uint16_t* out, hipStream_t stream);
+
+hipError_t launch_finalize_rmsnorm(const Routed& r, const uint16_t* residual,
+                                   const uint16_t* gamma, float eps,
+                                   uint16_t* residual_out, uint16_t* normed,
+                                   hipStream_t stream);
+
+hipError_t launch_finalize_quant(const Routed& r, uint8_t* out_e4m3,
+                                 uint8_t* scale_e8m0, hipStream_t stream);
+
+hipError_t launch_packed_decode(const int32_t* packed, int64_t n,
+                                int32_t* expert_ids, float* weights,
+                                hipStream_t stream);
+
+// Launch-shape limits the entry points enforce.
+constexpr int kWaveLanes = 64;
+constexpr int kVecElems = 8;                           // bf16 per 16-byte vector
+constexpr int kChunkCols = kWaveLanes * kVecElems;     // columns per wave pass
+constexpr int kWavesPerBlock = 4;                      // plain / quant kernels
+constexpr int kNormMaxThreads = 1024;                  // RMSNorm: one block per token
+constexpr int64_t kMaxUnits = (int64_t(1) << 31) - 1;  // (token, chunk) pairs
+
+}  // namespace moef

@@ -1,0 +1,193 @@
+/*
+ * moe_finalize.h - C ABI of the MI355X (gfx950) deferred MoE finalize library.
+ *
+ * The deferred finalize is the step after a grouped expert GEMM that was told
+ * not to combine its outputs: for every token it gathers that token's top_k
+ * un-weighted, expert-sorted rows of gemm2_out, weights each by its routing
+ * weight times the routed scaling factor, sums them in fp32, adds the
+ * shared-expert output and writes bf16. Optional fused epilogues add the
+ * residual and apply RMSNorm (emitting residual_out too), or quantize the
+ * result to FP8 E4M3 with one power-of-two (UE8M0) scale per 1 x 128 block.
+ *
+ * Sources (sglang pull-request pages):
+ *  - "Support deferred MoE finalize for MXFP4 and FP8 block-scale":
+ *    Motivation (the deferred top-k weighted combine, fused with the
+ *    shared-expert add) and Modifications item 2 (the routed scaling factor
+ *    is folded into the register-held expert weight; 1.0 is neutral), item 1
+ *    (the routing format is an explicit per-configuration choice).
+ *  - "[Kimi K2.5] Fuse deferred MoE finalize into next-layer AR + residual +
+ *    RMSNorm": Key modifications (the index map and weights are
+ *    [token, top_k]; a flat index caused out-of-bounds reads; workspaces are
+ *    sized before graph capture and never grow inside it) and "Numerics &
+ *    speed" (gathering from the padded permuted buffer; residual + RMSNorm
+ *    with residual_out; fp32 accumulation).
+ *  - "[FP8][MoE] Honor UE8M0 activation scales in Triton MoE": Motivation and
+ *    "More context" (power-of-two FP32 activation scales, FP8 range 448).
+ *  - "[Deepseek V4] Keep fp32 routing weights in the mxfp4 trtllm MoE":
+ *    PR description (packed word (expert_id << 16) | bf16(weight) versus
+ *    genuine fp32 weights; the finalize weight type is bf16 or float) and the
+ *    follow-up commit (reading fp32 weights as bf16 broke decoding).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller, row-major
+ *    and contiguous. bf16 values travel as raw bits in uint16_t, FP8 E4M3
+ *    codes and UE8M0 scale bytes as uint8_t. The library never allocates,
+ *    frees or keeps a pointer after the call returns, holds no mutable global
+ *    state, never synchronizes and never reads device memory from the host,
+ *    so every call may be captured into a HIP graph.
+ *  - `stream` is a hipStream_t passed as void* (NULL: the null stream). Work
+ *    is enqueued on it; the call returns without waiting.
+ *  - Return value: MOEF_OK (0) or a MOEF_ERR_* status. Every argument check
+ *    runs before any HIP runtime call; a failed check enqueues nothing.
+ *    MOEF_ERR_HIP reports a launch failure (hipGetLastError after the launch);
+ *    faults inside a kernel surface at the caller's next synchronization, as
+ *    in any HIP API.
+ *  - num_tokens == 0 is a successful no-op (pointers may then be NULL).
+ *  - Device error flag: `err_flag` is an optional device int32 that the
+ *    caller zeroes. The kernels OR MOEF_DEVERR_INDEX_OUT_OF_RANGE into it
+ *    when an index is >= num_rows; that slot is skipped. A negative index
+ *    marks a slot whose expert is not held here: it is skipped silently.
+ *  - Routing weights: exactly one of `topk_weights` (float32 [T, top_k]) and
+ *    `topk_packed` (int32 [T, top_k], (expert_id << 16) | bf16_bits(weight),
+ *    the id read with a logical shift and not used by the finalize) is
+ *    non-NULL, else MOEF_ERR_BAD_FORMAT. The two formats have distinct C
+ *    types so fp32 weights cannot be read as packed words by mistake.
+ *  - Arithmetic: w' = fp32(weight * routed_scaling_factor); acc = +0; for each
+ *    slot k in ascending order acc = acc + w'_k * x_k (separate fp32 multiply
+ *    and add, no fused multiply-add); acc = acc + shared; [acc = acc +
+ *    residual]; one round-to-nearest-even to bf16. The routed scaling factor
+ *    never scales the shared-expert output.
+ *  - Alignment: bf16 row tensors (gemm2_out, shared_out, out, residual,
+ *    residual_out, normed, gamma) 16-byte aligned; FP8 output 8-byte aligned;
+ *    index and weight tensors 4-byte aligned. Else MOEF_ERR_MISALIGNED.
+ *  - Aliasing: outputs may not overlap inputs or each other
+ *    (MOEF_ERR_BAD_ALIAS), except that residual_out may be exactly residual
+ *    (in-place residual update).
+ */
+#ifndef MOE_FINALIZE_H
+#define MOE_FINALIZE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOEF_ABI_VERSION 1
+#define MOEF_MAX_TOP_K 16            /* top_k must lie in [1, 16] */
+#define MOEF_MAX_HIDDEN 1048576      /* hidden must lie in [8, 2^20], multiple of 8 */
+#define MOEF_MAX_HIDDEN_RMSNORM 16384 /* the RMSNorm epilogue keeps a row on chip */
+#define MOEF_QUANT_BLOCK 128         /* the UE8M0 epilogue needs hidden % 128 == 0 */
+
+#define MOEF_DEVERR_INDEX_OUT_OF_RANGE 1
+
+enum moef_status {
+  MOEF_OK = 0,
+  MOEF_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  MOEF_ERR_BAD_SHAPE = 2,    /* negative count, hidden/top_k out of range */
+  MOEF_ERR_UNSUPPORTED = 3,  /* hidden not a multiple of 8 (or 128 for quant), too large */
+  MOEF_ERR_MISALIGNED = 4,   /* a pointer breaks the alignment rule */
+  MOEF_ERR_BAD_FORMAT = 5,   /* not exactly one routing-weight format given */
+  MOEF_ERR_BAD_ALIAS = 6,    /* an output overlaps an input or another output */
+  MOEF_ERR_HIP = 7           /* the HIP runtime rejected a launch */
+};
+
+/*
+ * moe_finalize - deferred finalize, bf16 out.
+ * ("Support deferred MoE finalize for MXFP4 and FP8 block-scale", Motivation
+ *  and Modifications item 2.)
+ *
+ *  gemm2_out   bf16 [num_rows, hidden]: expert-sorted, padded, un-weighted
+ *              expert outputs. Only rows named by the index map are read, so
+ *              padding may hold anything (NaN) and cost does not grow with
+ *              num_rows. May be NULL only if num_rows == 0.
+ *  num_rows    P >= 0, rows in gemm2_out.
+ *  expanded_idx_to_permuted_idx  int32 [num_tokens, top_k]: the gemm2_out
+ *              row of slot (t, k), at element t * top_k + k.
+ *  topk_weights / topk_packed    routing weights, exactly one non-NULL.
+ *  shared_out  bf16 [num_tokens, hidden] or NULL (no shared expert).
+ *  routed_scaling_factor         folded into every routed weight (1.0: none).
+ *  out         bf16 [num_tokens, hidden], written.
+ *  err_flag    optional device int32 (see conventions).
+ */
+int moe_finalize(const uint16_t* gemm2_out, int64_t num_rows,
+                 const int32_t* expanded_idx_to_permuted_idx,
+                 const float* topk_weights, const int32_t* topk_packed,
+                 const uint16_t* shared_out, float routed_scaling_factor,
+                 uint16_t* out,
+                 int64_t num_tokens, int64_t hidden, int32_t top_k,
+                 int32_t* err_flag, void* stream);
+
+/*
+ * moe_finalize_residual_rmsnorm - finalize + residual add + RMSNorm.
+ * ("[Kimi K2.5] Fuse deferred MoE finalize into next-layer AR + residual +
+ *  RMSNorm", Summary and "Numerics & speed"; on one GPU the all-reduce is the
+ *  identity.)
+ *
+ *  Routed arguments as moe_finalize, plus
+ *  residual      bf16 [num_tokens, hidden].
+ *  gamma         bf16 [hidden], the RMSNorm weight.
+ *  eps           added to the mean square inside the square root.
+ *  residual_out  bf16 [num_tokens, hidden] = bf16(acc + residual) with one
+ *                rounding; may be exactly `residual` (in place).
+ *  normed        bf16 [num_tokens, hidden] =
+ *                bf16(ro / sqrt(mean_h(ro^2) + eps) * gamma), ro being the
+ *                stored bf16 residual_out, computed in fp32.
+ *  hidden        at most MOEF_MAX_HIDDEN_RMSNORM.
+ */
+int moe_finalize_residual_rmsnorm(const uint16_t* gemm2_out, int64_t num_rows,
+                                  const int32_t* expanded_idx_to_permuted_idx,
+                                  const float* topk_weights, const int32_t* topk_packed,
+                                  const uint16_t* shared_out, float routed_scaling_factor,
+                                  const uint16_t* residual, const uint16_t* gamma, float eps,
+                                  uint16_t* residual_out, uint16_t* normed,
+                                  int64_t num_tokens, int64_t hidden, int32_t top_k,
+                                  int32_t* err_flag, void* stream);
+
+/*
+ * moe_finalize_quant_ue8m0 - finalize + FP8 E4M3 quantization with one
+ * power-of-two scale per 1 x 128 block along hidden.
+ * ("[FP8][MoE] Honor UE8M0 activation scales in Triton MoE", Motivation and
+ *  "More context".)
+ *
+ *  Routed arguments as moe_finalize, plus
+ *  out_e4m3    uint8 [num_tokens, hidden], OCP E4M3 ("e4m3fn", max 448) codes
+ *              of y * 2^-e, y being the bf16-rounded finalize result; nearest
+ *              even, subnormals kept, sign of zero kept.
+ *  scale_e8m0  uint8 [num_tokens, hidden / 128], the byte e + 127 where e is
+ *              the least integer with max|y over the block| <= 448 * 2^e,
+ *              clamped to [-127, 127] (an all-zero block gives e = -127).
+ *  hidden      a multiple of 128.
+ */
+int moe_finalize_quant_ue8m0(const uint16_t* gemm2_out, int64_t num_rows,
+                             const int32_t* expanded_idx_to_permuted_idx,
+                             const float* topk_weights, const int32_t* topk_packed,
+                             const uint16_t* shared_out, float routed_scaling_factor,
+                             uint8_t* out_e4m3, uint8_t* scale_e8m0,
+                             int64_t num_tokens, int64_t hidden, int32_t top_k,
+                             int32_t* err_flag, void* stream);
+
+/*
+ * moe_topk_packed_decode - split packed routing words.
+ * ("[Deepseek V4] Keep fp32 routing weights in the mxfp4 trtllm MoE",
+ *  PR description.)
+ *
+ *  packed      int32 [n], (expert_id << 16) | bf16_bits(weight).
+ *  expert_ids  int32 [n] = (uint32)packed >> 16, or NULL to skip.
+ *  weights     float32 [n] = the bf16 weight widened exactly, or NULL.
+ *  At least one output must be non-NULL. n == 0 is a no-op.
+ */
+int moe_topk_packed_decode(const int32_t* packed, int64_t n,
+                           int32_t* expert_ids, float* weights, void* stream);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* moe_finalize_status_string(int status);
+
+/* MOEF_ABI_VERSION of the built library. */
+int moe_finalize_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FINALIZE_H */

@@ -1,0 +1,161 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects bad arguments with the documented status
+before making any HIP call. Only rejected calls are made here, so nothing is
+ever launched. Pointers are fake, aligned or misaligned integers; the
+library never dereferences a pointer on the host."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_moe_finalize_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_finalize.h")
+
+OK, NULLP, SHAPE, UNSUP, MISAL, FMT, ALIAS = 0, 1, 2, 3, 4, 5, 6
+
+# fake device addresses, far apart and 256-byte aligned
+G2, IDX, W, PK, SH, OUT, RES, GAM, RO, NRM, Q, S, ERR = [0x10_0000_0000 * (i + 1) for i in range(13)]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmoe_finalize.so is not built (run python -m combine_moe_finalize_amd.build)")
+    return B.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"moe_finalize", "moe_finalize_residual_rmsnorm",
+                          "moe_finalize_quant_ue8m0", "moe_topk_packed_decode",
+                          "moe_finalize_status_string", "moe_finalize_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.moe_finalize_abi_version() == 1
+    for s in range(8):
+        txt = lib.moe_finalize_status_string(s)
+        assert txt and txt.decode()
+    assert lib.moe_finalize_status_string(99).decode() == "unknown status"
+
+
+def fin(lib, *, g2=G2, P=1024, idx=IDX, w=W, pk=None, sh=SH, rsf=2.5, out=OUT, T=4, H=4096,
+        k=8, err=None):
+    return lib.moe_finalize(g2, P, idx, w, pk, sh, rsf, out, T, H, k, err, None)
+
+
+def test_finalize_shape_rules(lib):
+    assert fin(lib, T=-1) == SHAPE
+    assert fin(lib, P=-1) == SHAPE
+    assert fin(lib, k=0) == SHAPE
+    assert fin(lib, k=17) == SHAPE
+    assert fin(lib, H=0) == SHAPE
+    assert fin(lib, H=4100) == UNSUP             # not a multiple of 8
+    assert fin(lib, H=(1 << 20) + 8) == UNSUP      # beyond the hidden limit
+    assert fin(lib, P=1 << 31) == UNSUP          # rows are named by int32
+
+
+def test_finalize_empty_batch_is_noop(lib):
+    assert fin(lib, T=0, g2=None, idx=None, w=None, sh=None, out=None) == OK
+
+
+def test_finalize_pointer_and_format_rules(lib):
+    assert fin(lib, idx=None) == NULLP
+    assert fin(lib, out=None) == NULLP
+    assert fin(lib, g2=None) == NULLP
+    assert fin(lib, g2=None, P=0) != NULLP       # P == 0 needs no buffer
+    assert fin(lib, w=None, pk=None) == FMT      # neither format
+    assert fin(lib, w=W, pk=PK) == FMT           # both formats
+
+
+def test_finalize_alignment_rules(lib):
+    assert fin(lib, g2=G2 + 8) == MISAL
+    assert fin(lib, sh=SH + 2) == MISAL
+    assert fin(lib, out=OUT + 4) == MISAL
+    assert fin(lib, idx=IDX + 2) == MISAL
+    assert fin(lib, w=W + 1) == MISAL
+    assert fin(lib, err=ERR + 2) == MISAL
+
+
+def test_finalize_alias_rules(lib):
+    assert fin(lib, out=G2 + 4096 * 2 * 10) == ALIAS       # inside gemm2_out
+    assert fin(lib, out=SH) == ALIAS
+    assert fin(lib, out=IDX - 16) == ALIAS                  # straddles idx
+    assert fin(lib, out=ERR, err=ERR) == ALIAS
+
+
+def rms(lib, *, T=16, H=7168, k=8, res=RES, gam=GAM, ro=RO, nrm=NRM, sh=SH, w=W, pk=None,
+        idx=IDX):
+    return lib.moe_finalize_residual_rmsnorm(G2, 4096, idx, w, pk, sh, 2.5, res, gam, 1e-6,
+                                             ro, nrm, T, H, k, None, None)
+
+
+def test_rmsnorm_rules(lib):
+    assert rms(lib, H=16392) == UNSUP               # beyond the on-chip row limit
+    assert rms(lib, H=16384, res=None) == NULLP     # 16384 itself is allowed
+    assert rms(lib, res=None) == NULLP
+    assert rms(lib, gam=None) == NULLP
+    assert rms(lib, nrm=None) == NULLP
+    assert rms(lib, gam=GAM + 2) == MISAL
+    assert rms(lib, ro=RES + 16) == ALIAS           # partial overlap with residual
+    assert rms(lib, nrm=RO) == ALIAS                # normed == residual_out
+    assert rms(lib, nrm=RES) == ALIAS
+    assert rms(lib, ro=GAM) == ALIAS
+    assert rms(lib, w=None, pk=None) == FMT
+    assert rms(lib, T=0, res=None, gam=None, ro=None, nrm=None, sh=None, w=None,
+               idx=None) == OK
+
+
+def qnt(lib, *, T=8, H=7168, k=8, q=Q, s=S, w=W, pk=None):
+    return lib.moe_finalize_quant_ue8m0(G2, 4096, IDX, w, pk, SH, 2.5, q, s, T, H, k, None, None)
+
+
+def test_quant_rules(lib):
+    assert qnt(lib, H=7168 + 8) == UNSUP            # not a multiple of 128
+    assert qnt(lib, q=None) == NULLP
+    assert qnt(lib, s=None) == NULLP
+    assert qnt(lib, q=Q + 4) == MISAL
+    assert qnt(lib, s=Q + 8 * 7168 - 1) == ALIAS    # scales overlap the codes
+    assert qnt(lib, q=G2) == ALIAS
+    assert qnt(lib, w=W, pk=PK) == FMT
+    assert qnt(lib, T=0, q=None, s=None) == OK
+
+
+def test_decode_rules(lib):
+    d = lib.moe_topk_packed_decode
+    assert d(PK, -1, IDX, W, None) == SHAPE
+    assert d(PK, 0, None, None, None) == OK
+    assert d(None, 8, IDX, W, None) == NULLP
+    assert d(PK, 8, None, None, None) == NULLP
+    assert d(PK + 2, 8, IDX, W, None) == MISAL
+    assert d(PK, 8, PK + 16, W, None) == ALIAS
+    assert d(PK, 8, IDX, IDX + 8, None) == ALIAS
+
+
+def test_binding_rejects_flat_and_wrong_dtypes():
+    import torch
+    g2 = torch.zeros((256, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="2-D"):
+        B.moe_finalize(g2, torch.zeros(16, dtype=torch.int32),
+                       topk_weights=torch.zeros(16, dtype=torch.float32))
+    idx = torch.zeros((8, 2), dtype=torch.int32)
+    with pytest.raises(TypeError, match="int32"):           # fp32 passed as packed
+        B.moe_finalize(g2, idx, topk_packed=torch.zeros((8, 2), dtype=torch.float32))
+    with pytest.raises(TypeError, match="float32"):         # packed passed as fp32
+        B.moe_finalize(g2, idx, topk_weights=torch.zeros((8, 2), dtype=torch.int32))
+    with pytest.raises(ValueError, match="exactly one"):
+        B.moe_finalize(g2, idx)
+    with pytest.raises(ValueError, match="GPU"):             # CPU tensors never run
+        B.moe_finalize(g2, idx, topk_weights=torch.zeros((8, 2), dtype=torch.float32))
