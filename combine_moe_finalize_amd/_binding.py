@@ -26,7 +26,7 @@ from typing import Optional
 
 import torch
 
-from .build import LIB_PATH
+from ._paths import LIB_PATH
 
 c_void_p = ctypes.c_void_p
 c_i64 = ctypes.c_int64
@@ -65,7 +65,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         return _lib
     p = path or LIB_PATH
     if not os.path.exists(p):
-        raise RuntimeError(f"{p} is missing: build it with `python -m combine_moe_finalize_amd.build`")
+        raise RuntimeError(f"{p} is missing: build it with `python combine_moe_finalize_amd/build.py`")
     lib = ctypes.CDLL(p)
     for name, args in _SIGNATURES.items():
         fn = getattr(lib, name)

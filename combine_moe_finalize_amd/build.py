@@ -1,6 +1,6 @@
 """Build the gfx950 shared library libmoe_finalize.so in-tree with hipcc.
 
-    python -m combine_moe_finalize_amd.build
+    python combine_moe_finalize_amd/build.py
 
 Flags: fp-contract off (the finalize's fp32 operation order is part of its
 contract: a separate multiply and add per gathered row, no fused
@@ -13,13 +13,11 @@ import shutil
 import subprocess
 import sys
 
-PKG = os.path.dirname(os.path.abspath(__file__))
-ROOT = os.path.dirname(PKG)
-CSRC = os.path.join(PKG, "csrc")
-INCLUDE = os.path.join(ROOT, "include")
-LIB_DIR = os.path.join(PKG, "_lib")
-LIB_NAME = "libmoe_finalize.so"
-LIB_PATH = os.path.join(LIB_DIR, LIB_NAME)
+try:
+    from ._paths import CSRC, INCLUDE, LIB_DIR, LIB_PATH
+except ImportError:            # run as a script
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from _paths import CSRC, INCLUDE, LIB_DIR, LIB_PATH
 
 SOURCES = ["moef_api.hip", "finalize_kernels.hip"]
 ARCH = "gfx950"

@@ -23,7 +23,7 @@ G2, IDX, W, PK, SH, OUT, RES, GAM, RO, NRM, Q, S, ERR = [0x10_0000_0000 * (i + 1
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(B.LIB_PATH):
-        pytest.fail("libmoe_finalize.so is not built (run python -m combine_moe_finalize_amd.build)")
+        pytest.fail("libmoe_finalize.so is not built (run python combine_moe_finalize_amd/build.py)")
     return B.load_library()
 
 

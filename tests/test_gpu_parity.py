@@ -344,6 +344,19 @@ def test_packed_decode():
     assert np.array_equal(w.cpu().numpy().reshape(-1).view(np.uint32), ow.view(np.uint32))
 
 
+def test_layout_invariance_on_gpu():
+    """The same rows in another order (token-ordered instead of expert-sorted,
+    no padding), with the map updated, give bitwise the same output."""
+    wl = W.config_workload(2)
+    announce("layout invariance T=256 H=7168")
+    a = run_finalize(wl)
+    wl.gemm2_out = wl.gemm2_out[wl.idx.reshape(-1)]
+    wl.idx = np.arange(wl.T * wl.top_k, dtype=np.int32).reshape(wl.T, wl.top_k)
+    b = run_finalize(wl)
+    assert_bits_equal(a, b, "token-ordered layout", zero_equal=False)
+    check_finalize(wl, b, what="token-ordered layout")
+
+
 # -------------------------------------------------------------- robustness
 def test_deterministic_and_canaries():
     wl = W.config_workload(1, 64)
