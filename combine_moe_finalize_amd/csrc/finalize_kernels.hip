@@ -16,8 +16,9 @@
 // columns and moves them with one 16-byte load per gathered row. The token's
 // top_k indices and weights are wave-uniform and land in scalar registers;
 // the weight (times the routed scaling factor) stays in a register for the
-// whole chunk. All top_k row loads and the shared / residual loads are issued
-// before the first add, so a lane has (top_k + 2) x 16 bytes in flight.
+// whole chunk. The shared / residual (and gamma) loads are issued first, since
+// they do not depend on the routing, then all top_k row loads, all before the
+// first add: a lane has up to (top_k + 2) x 16 bytes in flight.
 // Gathered rows are read exactly once and outputs are written once, so both
 // use non-temporal loads and stores (measured: the streaming stores alone take
 // the prefill launch from 197 to 187 microseconds).
@@ -27,9 +28,11 @@
 //    registers; sum of squares by cross-lane shuffles in the wave, then LDS
 //    across waves, summed in a fixed order so every lane sees the same value.
 //  * UE8M0 quant: a 1 x 128 block is 16 lanes x 8 columns, one DPP row; its
-//    absolute maximum takes four DPP row rotations, the power-of-two exponent
-//    comes from the maximum's bit fields, and each value is scaled exactly by
-//    ldexp and rounded to OCP E4M3 in integer arithmetic.
+//    absolute maximum is taken on bf16 bit patterns (packed 16-bit integer
+//    max, then four DPP row rotations), the power-of-two exponent comes from
+//    the maximum's bit fields, and gfx950's scaled fp32 converter divides each
+//    value by 2^e and rounds it to OCP E4M3 (nearest even), one op per pair.
+//  * bf16 rounding uses gfx950's packed fp32 -> bf16 converter (nearest even).
 //    ("[FP8][MoE] Honor UE8M0 activation scales in Triton MoE", Motivation
 //    and "More context".)
 
@@ -40,6 +43,10 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 // Kernel-side view of one routed call.
 struct GatherArgs {
@@ -62,11 +69,10 @@ struct GatherArgs {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest even; NaN -> quiet NaN keeping the sign.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two fp32 values -> one word of two bf16 (lo in bits 0..15), round to nearest
+// even, by gfx950's packed converter (NaN stays a quiet NaN with its sign).
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ void unpack8(const u32x4 v, float x[8]) {
@@ -76,12 +82,13 @@ __device__ __forceinline__ void unpack8(const u32x4 v, float x[8]) {
   x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
 }
 
-__device__ __forceinline__ u32x4 pack8_bits(const uint32_t b[8]) {
+// Eight fp32 values -> eight bf16 in one 16-byte vector (one rounding each).
+__device__ __forceinline__ u32x4 pack8_rne(const float x[8]) {
   u32x4 v;
-  v.x = b[0] | (b[1] << 16);
-  v.y = b[2] | (b[3] << 16);
-  v.z = b[4] | (b[5] << 16);
-  v.w = b[6] | (b[7] << 16);
+  v.x = bf16x2_rne(x[0], x[1]);
+  v.y = bf16x2_rne(x[2], x[3]);
+  v.z = bf16x2_rne(x[4], x[5]);
+  v.w = bf16x2_rne(x[6], x[7]);
   return v;
 }
 
@@ -116,22 +123,36 @@ __device__ __forceinline__ void load_route(const GatherArgs& a, int t,
     atomicOr(a.err, MOEF_DEVERR_INDEX_OUT_OF_RANGE);
 }
 
-// acc[0..7] for columns [8*col, 8*col + 8) of token t: the weighted sum of the
-// gathered rows, then + shared, then + residual (when given), each in fp32.
+// The operands of one column vector that do not depend on the routing: the
+// shared-expert and residual vectors. They are issued before the token's
+// indices arrive, so their latency overlaps the index fetch.
+struct Side {
+  u32x4 s;
+  u32x4 r;
+};
+
+__device__ __forceinline__ Side load_side(const GatherArgs& a, int t, int64_t col,
+                                          const u32x4* residual_row) {
+  Side d;
+  d.s = u32x4{0u, 0u, 0u, 0u};
+  d.r = u32x4{0u, 0u, 0u, 0u};
+  if (a.shared != nullptr) d.s = __builtin_nontemporal_load(a.shared + (int64_t)t * a.h8 + col);
+  if (residual_row != nullptr) d.r = __builtin_nontemporal_load(residual_row + col);
+  return d;
+}
+
+// acc[0..7] for columns [8*col, 8*col + 8): the weighted sum of the gathered
+// rows, then + shared, then + residual (when given), each step in fp32.
 template <int KMAX, bool EXACT>
-__device__ __forceinline__ void finalize_acc(const GatherArgs& a, int t, int64_t col,
+__device__ __forceinline__ void finalize_acc(const GatherArgs& a, int64_t col,
                                              const int32_t row[KMAX], const float w[KMAX],
-                                             const u32x4* residual_row, float acc[8]) {
+                                             const Side& d, bool has_residual, float acc[8]) {
   u32x4 v[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     if ((EXACT || j < a.k) && row[j] >= 0)
       v[j] = __builtin_nontemporal_load(a.g2 + (int64_t)row[j] * a.h8 + col);
   }
-  u32x4 s = {0u, 0u, 0u, 0u};
-  u32x4 r = {0u, 0u, 0u, 0u};
-  if (a.shared != nullptr) s = __builtin_nontemporal_load(a.shared + (int64_t)t * a.h8 + col);
-  if (residual_row != nullptr) r = residual_row[col];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 #pragma unroll
@@ -145,13 +166,13 @@ __device__ __forceinline__ void finalize_acc(const GatherArgs& a, int t, int64_t
   }
   if (a.shared != nullptr) {
     float x[8];
-    unpack8(s, x);
+    unpack8(d.s, x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = acc[e] + x[e];
   }
-  if (residual_row != nullptr) {
+  if (has_residual) {
     float x[8];
-    unpack8(r, x);
+    unpack8(d.r, x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = acc[e] + x[e];
   }
@@ -171,16 +192,14 @@ finalize_kernel(GatherArgs a, u32x4* __restrict__ out) {
   const bool active = colv < a.h8;
   const int64_t col = active ? colv : a.h8 - 1;   // keep every lane's loads in bounds
 
+  const Side d = load_side(a, t, col, nullptr);
   int32_t row[KMAX];
   float w[KMAX];
   load_route<KMAX, EXACT>(a, t, row, w);
   float acc[8];
-  finalize_acc<KMAX, EXACT>(a, t, col, row, w, nullptr, acc);
+  finalize_acc<KMAX, EXACT>(a, col, row, w, d, false, acc);
 
-  uint32_t b[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) b[e] = bf16_rne(acc[e]);
-  if (active) __builtin_nontemporal_store(pack8_bits(b), out + (int64_t)t * a.h8 + colv);
+  if (active) __builtin_nontemporal_store(pack8_rne(acc), out + (int64_t)t * a.h8 + colv);
 }
 
 // ------------------------------------------------------- residual + RMSNorm
@@ -202,10 +221,20 @@ finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __rest
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
+  const u32x4* res_row = residual + (int64_t)t * a.h8;
+  // row-independent operands first: shared, residual and gamma vectors
+  Side d[CPT];
+  u32x4 gv[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int colv = threadIdx.x + i * nthreads;
+    const int64_t col = colv < a.h8 ? colv : a.h8 - 1;
+    d[i] = load_side(a, t, col, res_row);
+    gv[i] = gamma[col];
+  }
   int32_t row[KMAX];
   float w[KMAX];
   load_route<KMAX, EXACT>(a, t, row, w);
-  const u32x4* res_row = residual + (int64_t)t * a.h8;
 
   float ro[CPT][8];
   float ss = 0.0f;
@@ -215,15 +244,11 @@ finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __rest
     const bool active = colv < a.h8;
     const int64_t col = active ? colv : a.h8 - 1;
     float acc[8];
-    finalize_acc<KMAX, EXACT>(a, t, col, row, w, res_row, acc);
-    uint32_t b[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      b[e] = bf16_rne(acc[e]);
-      ro[i][e] = __uint_as_float(b[e] << 16);
-    }
+    finalize_acc<KMAX, EXACT>(a, col, row, w, d[i], true, acc);
+    const u32x4 rb = pack8_rne(acc);
+    unpack8(rb, ro[i]);                     // the stored bf16 residual_out
     if (active) {
-      __builtin_nontemporal_store(pack8_bits(b), residual_out + (int64_t)t * a.h8 + colv);
+      __builtin_nontemporal_store(rb, residual_out + (int64_t)t * a.h8 + colv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = ss + ro[i][e] * ro[i][e];
     }
@@ -240,11 +265,11 @@ finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __rest
     const int colv = threadIdx.x + i * nthreads;
     if (colv < a.h8) {
       float g[8];
-      unpack8(gamma[colv], g);
-      uint32_t b[8];
+      unpack8(gv[i], g);
+      float n[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) b[e] = bf16_rne((ro[i][e] * inv) * g[e]);
-      __builtin_nontemporal_store(pack8_bits(b), normed + (int64_t)t * a.h8 + colv);
+      for (int e = 0; e < 8; ++e) n[e] = (ro[i][e] * inv) * g[e];
+      __builtin_nontemporal_store(pack8_rne(n), normed + (int64_t)t * a.h8 + colv);
     }
   }
 }
@@ -252,43 +277,54 @@ finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __rest
 // ------------------------------------------------------- UE8M0 / E4M3 quant
 
 // Largest value across the 16 lanes of a DPP row (every lane gets it).
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xF, 0xF, false)));
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));   // row_ror:8
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));   // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x122, 0xF, 0xF, false));   // row_ror:2
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x121, 0xF, 0xF, false));   // row_ror:1
   return v;
 }
 
-// Least e with amax <= 448 * 2^e, clamped to [-127, 127]. With
-// amax = 2^E * 1.f and 448 = 2^8 * 1.75: e = E - 8, plus one when 1.f > 1.75
-// (fraction field above 0x600000). Zero and subnormal amax clamp to -127
-// (every subnormal is below 448 * 2^-127); inf / NaN give 127.
-__device__ __forceinline__ int ue8m0_exponent(float amax) {
-  const uint32_t b = __float_as_uint(amax);
-  const int ef = (int)(b >> 23);
+// Largest |y| of the eight bf16 values in v, as bf16 bits: with the sign
+// cleared, bf16 bit patterns order like their magnitudes (NaN above inf).
+__device__ __forceinline__ uint32_t absmax8_bits(const u32x4 v) {
+  const u16x2 a = __builtin_elementwise_max(__builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu),
+                                            __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu));
+  const u16x2 b = __builtin_elementwise_max(__builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu),
+                                            __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu));
+  const u16x2 m = __builtin_elementwise_max(a, b);
+  return m.x > m.y ? m.x : m.y;
+}
+
+// Least e with amax <= 448 * 2^e, clamped to [-127, 127], from the bf16 bits
+// of amax >= 0. With amax = 2^E * 1.f and 448 = 2^8 * 1.75: e = E - 8, plus one
+// when 1.f > 1.75 (7-bit fraction above 0x60). Zero and subnormal amax clamp to
+// -127 (every subnormal is below 448 * 2^-127); inf / NaN give 127.
+__device__ __forceinline__ int ue8m0_exponent(uint32_t amax_bf16) {
+  const int ef = (int)(amax_bf16 >> 7);
   if (ef == 0) return -127;
   if (ef >= 255) return 127;
-  const int e = ef - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  const int e = ef - 135 + ((amax_bf16 & 0x7Fu) > 0x60u ? 1 : 0);
   return e < -127 ? -127 : e;
 }
 
-// OCP E4M3 ("e4m3fn": bias 7, max 448, NaN S.1111.111) code of s, nearest
-// even, subnormals kept, sign of zero kept. Magnitudes rounding above 448 and
-// NaN give the NaN code.
-__device__ __forceinline__ uint32_t e4m3_rne(float s) {
-  const uint32_t u = __float_as_uint(s);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x3C800000u) {                               // |s| >= 2^-6: normal
-    a = (a + 0x7FFFFu + ((a >> 20) & 1u)) & 0xFFF00000u; // 3 fraction bits, ties even
-    code = (a > 0x43E00000u) ? 0x7Fu                     // beyond 448 (or inf / NaN)
-                             : ((((a >> 23) - 120u) << 3) | ((a >> 20) & 7u));
-  } else {                                              // subnormal: multiples of 2^-9
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);   // 0..8, exact scaling
-  }
-  return code | sign;
+// 2^e as an fp32 scale operand; 2^-127 is the subnormal 0x00400000.
+__device__ __forceinline__ float ue8m0_scale(int e) {
+  return __uint_as_float(e > -127 ? (uint32_t)(e + 127) << 23 : 0x00400000u);
+}
+
+// Eight bf16 values y -> eight OCP E4M3 codes of y / 2^e (round to nearest
+// even, subnormals and the sign of zero kept, beyond 448 / NaN -> NaN code),
+// two per gfx950 scaled fp32 converter op, in column order. (The scale only
+// ever is an exact power of two, so the division is exact.)
+__device__ __forceinline__ u32x2 e4m3x8_scaled(const u32x4 y, float scale) {
+  float f[8];
+  unpack8(y, f);
+  s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((s16x2){0, 0}, f[0], f[1], scale, false);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, f[2], f[3], scale, true);
+  s16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((s16x2){0, 0}, f[4], f[5], scale, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, f[6], f[7], scale, true);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 template <int KMAX, bool EXACT>
@@ -303,28 +339,17 @@ finalize_quant_kernel(GatherArgs a, u32x2* __restrict__ out_q, uint8_t* __restri
   const bool active = colv < a.h8;       // h8 % 16 == 0: whole DPP rows agree
   const int64_t col = active ? colv : a.h8 - 1;
 
+  const Side d = load_side(a, t, col, nullptr);
   int32_t row[KMAX];
   float w[KMAX];
   load_route<KMAX, EXACT>(a, t, row, w);
   float acc[8];
-  finalize_acc<KMAX, EXACT>(a, t, col, row, w, nullptr, acc);
+  finalize_acc<KMAX, EXACT>(a, col, row, w, d, false, acc);
 
-  float y[8];
-  float amax = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    y[e] = __uint_as_float(bf16_rne(acc[e]) << 16);   // the bf16 finalize result
-    amax = fmaxf(amax, fabsf(y[e]));
-  }
-  if (!active) amax = 0.0f;
-  amax = row16_max(amax);
+  const u32x4 y = pack8_rne(acc);                    // the bf16 finalize result
+  const uint32_t amax = row16_max(active ? absmax8_bits(y) : 0u);
   const int ex = ue8m0_exponent(amax);
-  u32x2 q = {0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    q.x |= e4m3_rne(ldexpf(y[e], -ex)) << (8 * e);
-    q.y |= e4m3_rne(ldexpf(y[e + 4], -ex)) << (8 * e);
-  }
+  const u32x2 q = e4m3x8_scaled(y, ue8m0_scale(ex));
   if (active) {
     __builtin_nontemporal_store(q, out_q + (int64_t)t * a.h8 + colv);
     if ((lane & 15) == 0) scale[(int64_t)t * (a.h8 >> 4) + (colv >> 4)] = (uint8_t)(ex + 127);

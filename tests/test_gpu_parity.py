@@ -216,6 +216,28 @@ def test_quant_exhaustive_codes_and_exponents():
     assert_bits_equal(q, oq, "exhaustive codes")
 
 
+def test_bf16_rounding_of_arbitrary_fp32():
+    """top_k 1, every gathered row 1.0, rsf 1, no shared output: out = bf16(w)
+    for the fp32 weight w, so every fp32 -> bf16 rounding decision (ties both
+    ways, subnormals, overflow to inf) is checked against the oracle."""
+    rng = np.random.default_rng(81)
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    bits = np.concatenate([hi | 0x8000, hi | 0x7FFF, hi | 0x8001, hi,
+                           rng.integers(0, 2 ** 32, 200_000, dtype=np.uint64).astype(np.uint32)])
+    w = bits.view(np.float32)
+    w = w[~np.isnan(w)].reshape(-1, 1)
+    T, H = w.shape[0], 8
+    g2 = np.full((128, H), W.NAN_BF16, dtype=np.uint16)
+    g2[5] = 0x3F80                                     # 1.0
+    idx = np.full((T, 1), 5, dtype=np.int32)
+    announce(f"bf16 rounding of {T} fp32 values")
+    out = M.moe_finalize(d_bf16(g2), d_i32(idx), topk_weights=d_f32(w), routed_scaling_factor=1.0)
+    torch.cuda.synchronize()
+    got = h_bits(out)
+    want, _ = O.finalize_mirror(g2, idx, weights_f32=w, rsf=1.0)
+    assert_bits_equal(got, want, "bf16 rounding")
+
+
 # ------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("k", [1, 2, 3, 5, 6, 7, 9, 16])
 def test_every_top_k_path(k):
