@@ -9,9 +9,10 @@ code; only the seeded input generators serve both).
 ``formats``  - bf16 / OCP E4M3 / UE8M0 helpers from the format definitions.
 ``finalize`` - finalize, residual + RMSNorm and UE8M0 quant, in an fp64
                "truth" mode and an fp32 "mirror" mode.
+``routing``  - the sigmoid top-k gate and packed-word producer that feed it.
 
 Every function is pinned by CPU tests to something other than itself
 (closed forms, exhaustive enumeration, exact rational arithmetic, library
 routines, invariants); see ``tests/test_oracle_*.py``.
 """
-from . import formats, finalize  # noqa: F401
+from . import formats, finalize, routing  # noqa: F401
