@@ -22,7 +22,8 @@ Printed: one JSON line with
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload,
   sweep      microseconds per call and GB/s for the other workload shapes
              (decode T=1..256, packed vs fp32 routing, residual + RMSNorm,
-             packed decode): per-call HIP-event times (which include a few
+             packed decode, the routing gate; for the gate the "H" field holds
+             the expert count E): per-call HIP-event times (which include a few
              microseconds of event overhead), warm and cold (after streaming
              a 1 GiB buffer through the caches); the sustained per-call time
              of 100 back-to-back calls; and the per-call time of 20 calls
@@ -240,6 +241,15 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
         measure("residual_rmsnorm", T, wl.H, wl.top_k, bytes_rmsnorm(T, wl.H, wl.top_k),
                 lambda: M.moe_finalize_residual_rmsnorm(**kw, **ex, residual_out=ro, normed=nm),
                 iters_big if T >= 1024 else iters_small)
+    for T in (1, 256, 8192):
+        E, k = 256, 8
+        lg = torch.from_numpy(W.router_logits(T, E, seed=T)).to("cuda:0")
+        gi = torch.empty((T, k), dtype=torch.int32, device="cuda:0")
+        gw = torch.empty((T, k), dtype=torch.float32, device="cuda:0")
+        gp = torch.empty((T, k), dtype=torch.int32, device="cuda:0")
+        measure("topk_sigmoid_gate", T, E, k, T * (4 * E + 12 * k),
+                lambda: M.moe_topk_sigmoid_gate(lg, k, topk_ids=gi, topk_weights=gw,
+                                                topk_packed=gp), iters_small)
     n = 8192 * 8
     pk = torch.from_numpy(W.config_workload(0).packed.reshape(-1).repeat(n // 2)).to("cuda:0")
     ids = torch.empty_like(pk)

@@ -14,5 +14,6 @@ from ._binding import (  # noqa: F401
     moe_finalize_quant_ue8m0,
     moe_finalize_residual_rmsnorm,
     moe_topk_packed_decode,
+    moe_topk_sigmoid_gate,
     status_string,
 )

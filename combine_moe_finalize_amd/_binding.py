@@ -45,6 +45,8 @@ _SIGNATURES = {
     "moe_finalize_quant_ue8m0": _ROUTED + [c_void_p, c_void_p, c_i64, c_i64, c_i32,
                                            c_void_p, c_void_p],
     "moe_topk_packed_decode": [c_void_p, c_i64, c_void_p, c_void_p, c_void_p],
+    "moe_topk_sigmoid_gate": [c_void_p, c_i64, c_i32, c_i32, c_void_p, c_void_p, c_void_p,
+                              c_void_p],
     "moe_finalize_status_string": [ctypes.c_int],
     "moe_finalize_abi_version": [],
 }
@@ -256,3 +258,36 @@ def moe_topk_packed_decode(topk_packed: torch.Tensor, *,
                                                _stream(device))
     _check("moe_topk_packed_decode", st)
     return expert_ids, weights
+
+
+def moe_topk_sigmoid_gate(router_logits: torch.Tensor, top_k: int, *,
+                          topk_ids: Optional[torch.Tensor] = None,
+                          topk_weights: Optional[torch.Tensor] = None,
+                          topk_packed: Optional[torch.Tensor] = None,
+                          want_weights: bool = True, want_packed: bool = True):
+    """(topk_ids int32, topk_weights float32 or None, topk_packed int32 or
+    None), each [T, top_k], from float32 router logits [T, E]."""
+    if not isinstance(router_logits, torch.Tensor) or router_logits.dim() != 2:
+        raise ValueError("router_logits must be a 2-D [tokens, experts] tensor")
+    T, E = router_logits.shape
+    device = router_logits.device
+    _tensor(router_logits, "router_logits", torch.float32, (T, E))
+    shape = (T, int(top_k))
+    if topk_ids is None:
+        topk_ids = torch.empty(shape, dtype=torch.int32, device=device)
+    if topk_weights is None and want_weights:
+        topk_weights = torch.empty(shape, dtype=torch.float32, device=device)
+    if topk_packed is None and want_packed:
+        topk_packed = torch.empty(shape, dtype=torch.int32, device=device)
+    _tensor(topk_ids, "topk_ids", torch.int32, shape)
+    if topk_weights is not None:
+        _tensor(topk_weights, "topk_weights", torch.float32, shape)
+    if topk_packed is not None:
+        _tensor(topk_packed, "topk_packed", torch.int32, shape)
+    _on_device(device, router_logits=router_logits, topk_ids=topk_ids,
+               topk_weights=topk_weights, topk_packed=topk_packed)
+    st = load_library().moe_topk_sigmoid_gate(_ptr(router_logits), T, E, int(top_k),
+                                              _ptr(topk_ids), _ptr(topk_weights),
+                                              _ptr(topk_packed), _stream(device))
+    _check("moe_topk_sigmoid_gate", st)
+    return topk_ids, topk_weights, topk_packed

@@ -225,4 +225,29 @@ int moe_topk_packed_decode(const int32_t* packed, int64_t n, int32_t* expert_ids
                                                static_cast<hipStream_t>(stream)));
 }
 
+int moe_topk_sigmoid_gate(const float* router_logits, int64_t num_tokens, int32_t num_experts,
+                          int32_t top_k, int32_t* topk_ids, float* topk_weights,
+                          int32_t* topk_packed, void* stream) {
+  if (num_tokens < 0 || num_experts < 1 || top_k < 1 || top_k > MOEF_MAX_TOP_K ||
+      top_k > num_experts)
+    return MOEF_ERR_BAD_SHAPE;
+  if (num_experts > MOEF_MAX_GATE_EXPERTS) return MOEF_ERR_UNSUPPORTED;
+  if (num_tokens > (int64_t)INT32_MAX - 4) return MOEF_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOEF_OK;
+  if (router_logits == nullptr || topk_ids == nullptr) return MOEF_ERR_NULL_POINTER;
+  if (!aligned(router_logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
+      !aligned(topk_packed, 4))
+    return MOEF_ERR_MISALIGNED;
+  const int64_t lb = num_tokens * num_experts * 4;
+  const int64_t ob = num_tokens * top_k * 4;
+  const Span in[1] = {{router_logits, lb}};
+  if (overlaps_any(topk_ids, ob, in, 1) || overlaps_any(topk_weights, ob, in, 1) ||
+      overlaps_any(topk_packed, ob, in, 1) || overlap(topk_ids, ob, topk_weights, ob) ||
+      overlap(topk_ids, ob, topk_packed, ob) || overlap(topk_weights, ob, topk_packed, ob))
+    return MOEF_ERR_BAD_ALIAS;
+  return hip_status(moef::launch_topk_sigmoid_gate(router_logits, num_tokens, num_experts,
+                                                   top_k, topk_ids, topk_weights, topk_packed,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -40,6 +40,10 @@ hipError_t launch_packed_decode(const int32_t* packed, int64_t n,
                                 int32_t* expert_ids, float* weights,
                                 hipStream_t stream);
 
+hipError_t launch_topk_sigmoid_gate(const float* logits, int64_t tokens, int32_t experts,
+                                    int32_t top_k, int32_t* ids, float* weights,
+                                    int32_t* packed, hipStream_t stream);
+
 // Launch-shape limits the entry points enforce.
 constexpr int kWaveLanes = 64;
 constexpr int kVecElems = 8;                           // bf16 per 16-byte vector

@@ -179,6 +179,12 @@ def make_workload(T: int, H: int, E: int, top_k: int, *, rsf: float = 2.5,
                     residual=residual, gamma=gamma, eps=eps)
 
 
+def router_logits(T: int, E: int, seed: int, scale: float = 1.0) -> np.ndarray:
+    """float32 router logits [T, E], scale * N(0,1), for the gate."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 5])))
+    return (g.standard_normal((T, E), dtype=np.float32) * np.float32(scale))
+
+
 # The five synthetic workload families (sizes as in the published setup).
 CONFIGS = {
     0: dict(name="tiny", Ts=(1,), H=1024, E=16, top_k=2),

@@ -78,6 +78,7 @@ extern "C" {
 #define MOEF_MAX_HIDDEN 1048576      /* hidden must lie in [8, 2^20], multiple of 8 */
 #define MOEF_MAX_HIDDEN_RMSNORM 16384 /* the RMSNorm epilogue keeps a row on chip */
 #define MOEF_QUANT_BLOCK 128         /* the UE8M0 epilogue needs hidden % 128 == 0 */
+#define MOEF_MAX_GATE_EXPERTS 512    /* the gate keeps a token's logits in registers */
 
 #define MOEF_DEVERR_INDEX_OUT_OF_RANGE 1
 
@@ -179,6 +180,31 @@ int moe_finalize_quant_ue8m0(const uint16_t* gemm2_out, int64_t num_rows,
  */
 int moe_topk_packed_decode(const int32_t* packed, int64_t n,
                            int32_t* expert_ids, float* weights, void* stream);
+
+/*
+ * moe_topk_sigmoid_gate - the routing front-end that feeds the finalize:
+ * top_k experts per token from router logits, with fp32 weights and/or the
+ * packed words. ("[Deepseek V4] Keep fp32 routing weights in the mxfp4
+ * trtllm MoE", PR description: the gate produces fp32 routing weights, and
+ * packing them into (expert_id << 16) | bf16(weight) truncates them.)
+ *
+ *  router_logits  float32 [num_tokens, num_experts].
+ *  num_experts    E in [1, MOEF_MAX_GATE_EXPERTS].
+ *  top_k          in [1, min(E, MOEF_MAX_TOP_K)].
+ *  topk_ids       int32 [num_tokens, top_k], written: the top_k largest logits
+ *                 (= the top_k sigmoid scores), in descending order; ties go to
+ *                 the lower expert id; NaN logits rank below every number.
+ *  topk_weights   float32 [num_tokens, top_k] or NULL: sigmoid(logit) of each
+ *                 chosen expert divided by their sum (fp32; the routed scaling
+ *                 factor is not applied here).
+ *  topk_packed    int32 [num_tokens, top_k] or NULL: (id << 16) | bf16 bits of
+ *                 the weight, rounded to nearest even.
+ *  num_tokens == 0 is a no-op.
+ */
+int moe_topk_sigmoid_gate(const float* router_logits, int64_t num_tokens,
+                          int32_t num_experts, int32_t top_k,
+                          int32_t* topk_ids, float* topk_weights, int32_t* topk_packed,
+                          void* stream);
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* moe_finalize_status_string(int status);

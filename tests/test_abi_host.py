@@ -38,7 +38,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"moe_finalize", "moe_finalize_residual_rmsnorm",
                           "moe_finalize_quant_ue8m0", "moe_topk_packed_decode",
-                          "moe_finalize_status_string", "moe_finalize_abi_version"}
+                          "moe_finalize_status_string", "moe_finalize_abi_version",
+                          "moe_topk_sigmoid_gate"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -159,3 +160,20 @@ def test_binding_rejects_flat_and_wrong_dtypes():
         B.moe_finalize(g2, idx)
     with pytest.raises(ValueError, match="GPU"):             # CPU tensors never run
         B.moe_finalize(g2, idx, topk_weights=torch.zeros((8, 2), dtype=torch.float32))
+
+
+def test_gate_rules(lib):
+    g = lib.moe_topk_sigmoid_gate
+    LG, ID, WT, PKD = G2, IDX, W, PK
+    assert g(LG, -1, 256, 8, ID, WT, PKD, None) == SHAPE
+    assert g(LG, 4, 0, 1, ID, WT, PKD, None) == SHAPE
+    assert g(LG, 4, 256, 0, ID, WT, PKD, None) == SHAPE
+    assert g(LG, 4, 256, 17, ID, WT, PKD, None) == SHAPE       # top_k above 16
+    assert g(LG, 4, 4, 5, ID, WT, PKD, None) == SHAPE          # top_k above E
+    assert g(LG, 4, 513, 8, ID, WT, PKD, None) == UNSUP        # E above the limit
+    assert g(LG, 0, 256, 8, None, None, None, None) == OK
+    assert g(None, 4, 256, 8, ID, WT, PKD, None) == NULLP
+    assert g(LG, 4, 256, 8, None, WT, PKD, None) == NULLP      # ids are required
+    assert g(LG + 2, 4, 256, 8, ID, WT, PKD, None) == MISAL
+    assert g(LG, 4, 256, 8, LG + 64, WT, PKD, None) == ALIAS   # ids inside the logits
+    assert g(LG, 4, 256, 8, ID, ID + 16, PKD, None) == ALIAS   # weights overlap ids
