@@ -10,9 +10,11 @@ code; only the seeded input generators serve both).
 ``finalize`` - finalize, residual + RMSNorm and UE8M0 quant, in an fp64
                "truth" mode and an fp32 "mirror" mode.
 ``routing``  - the sigmoid top-k gate and packed-word producer that feed it.
+``act_quant`` - standalone 1 x 128 FP8 activation quant, power-of-two
+               (UE8M0) and continuous (amax / 448) scale policies.
 
 Every function is pinned by CPU tests to something other than itself
 (closed forms, exhaustive enumeration, exact rational arithmetic, library
 routines, invariants); see ``tests/test_oracle_*.py``.
 """
-from . import formats, finalize, routing  # noqa: F401
+from . import act_quant, finalize, formats, routing  # noqa: F401
