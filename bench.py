@@ -22,7 +22,8 @@ Printed: one JSON line with
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload,
   sweep      microseconds per call and GB/s for the other workload shapes
              (decode T=1..256, packed vs fp32 routing, residual + RMSNorm,
-             packed decode, the routing gate; for the gate the "H" field holds
+             packed decode, the routing gate, standalone FP8 activation
+             quant in both scale policies; for the gate the "H" field holds
              the expert count E): per-call HIP-event times (which include a few
              microseconds of event overhead), warm and cold (after streaming
              a 1 GiB buffer through the caches); the sustained per-call time
@@ -45,7 +46,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "combine_moe_finalize_amd", "csrc", "finalize_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "combine_moe_finalize_amd", "csrc", f)
+                  for f in ("finalize_kernels.hip", "device_common.h")]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_quant_T8192_H7168_counters.json")
 
 
@@ -63,8 +65,12 @@ def bytes_quant(T, H, k, shared=True):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 over the sources the timed kernel is built from."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def counters_traffic():
@@ -250,6 +256,17 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
         measure("topk_sigmoid_gate", T, E, k, T * (4 * E + 12 * k),
                 lambda: M.moe_topk_sigmoid_gate(lg, k, topk_ids=gi, topk_weights=gw,
                                                 topk_packed=gp), iters_small)
+    for T in (16, 8192):
+        H = 7168
+        xa = torch.from_numpy(W.activations(T, H, seed=T).view(np.int16)).view(
+            torch.bfloat16).to("cuda:0")
+        aq = torch.empty((T, H), dtype=torch.uint8, device="cuda:0")
+        a8 = torch.empty((T, H // 128), dtype=torch.uint8, device="cuda:0")
+        af = torch.empty((T, H // 128), dtype=torch.float32, device="cuda:0")
+        measure("act_quant_ue8m0", T, H, 0, T * (3 * H + H // 128),
+                lambda: M.moe_act_quant_fp8_ue8m0(xa, out_e4m3=aq, scale_e8m0=a8), iters_small)
+        measure("act_quant_amax", T, H, 0, T * (3 * H + 4 * (H // 128)),
+                lambda: M.moe_act_quant_fp8_amax(xa, out_e4m3=aq, scale_f32=af), iters_small)
     n = 8192 * 8
     pk = torch.from_numpy(W.config_workload(0).packed.reshape(-1).repeat(n // 2)).to("cuda:0")
     ids = torch.empty_like(pk)

@@ -10,6 +10,8 @@ from ._binding import (  # noqa: F401
     MoeFinalizeError,
     abi_version,
     load_library,
+    moe_act_quant_fp8_amax,
+    moe_act_quant_fp8_ue8m0,
     moe_finalize,
     moe_finalize_quant_ue8m0,
     moe_finalize_residual_rmsnorm,

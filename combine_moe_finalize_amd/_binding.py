@@ -47,6 +47,8 @@ _SIGNATURES = {
     "moe_topk_packed_decode": [c_void_p, c_i64, c_void_p, c_void_p, c_void_p],
     "moe_topk_sigmoid_gate": [c_void_p, c_i64, c_i32, c_i32, c_void_p, c_void_p, c_void_p,
                               c_void_p],
+    "moe_act_quant_fp8_ue8m0": [c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_void_p],
+    "moe_act_quant_fp8_amax": [c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_void_p],
     "moe_finalize_status_string": [ctypes.c_int],
     "moe_finalize_abi_version": [],
 }
@@ -291,3 +293,38 @@ def moe_topk_sigmoid_gate(router_logits: torch.Tensor, top_k: int, *,
                                               _ptr(topk_packed), _stream(device))
     _check("moe_topk_sigmoid_gate", st)
     return topk_ids, topk_weights, topk_packed
+
+
+def _act_quant(fn_name, x, out_e4m3, scale, scale_dtype):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D [tokens, hidden] tensor")
+    T, H = x.shape
+    if H % QUANT_BLOCK:
+        raise ValueError("hidden must be a multiple of 128")
+    device = x.device
+    _tensor(x, "x", torch.bfloat16, (T, H))
+    if out_e4m3 is None:
+        out_e4m3 = torch.empty((T, H), dtype=torch.uint8, device=device)
+    if out_e4m3.dtype == torch.float8_e4m3fn:
+        out_e4m3 = out_e4m3.view(torch.uint8)
+    if scale is None:
+        scale = torch.empty((T, H // QUANT_BLOCK), dtype=scale_dtype, device=device)
+    _tensor(out_e4m3, "out_e4m3", torch.uint8, (T, H))
+    _tensor(scale, "scale", scale_dtype, (T, H // QUANT_BLOCK))
+    _on_device(device, x=x, out_e4m3=out_e4m3, scale=scale)
+    st = getattr(load_library(), fn_name)(_ptr(x), T, H, _ptr(out_e4m3), _ptr(scale),
+                                          _stream(device))
+    _check(fn_name, st)
+    return out_e4m3, scale
+
+
+def moe_act_quant_fp8_ue8m0(x: torch.Tensor, *, out_e4m3: Optional[torch.Tensor] = None,
+                            scale_e8m0: Optional[torch.Tensor] = None):
+    """(codes uint8 [T, H], scale bytes uint8 [T, H/128]): power-of-two scales."""
+    return _act_quant("moe_act_quant_fp8_ue8m0", x, out_e4m3, scale_e8m0, torch.uint8)
+
+
+def moe_act_quant_fp8_amax(x: torch.Tensor, *, out_e4m3: Optional[torch.Tensor] = None,
+                           scale_f32: Optional[torch.Tensor] = None):
+    """(codes uint8 [T, H], scales float32 [T, H/128]): s = amax / 448."""
+    return _act_quant("moe_act_quant_fp8_amax", x, out_e4m3, scale_f32, torch.float32)

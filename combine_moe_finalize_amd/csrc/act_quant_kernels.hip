@@ -1,0 +1,85 @@
+// gfx950 standalone FP8 activation quantization, 1 x 128 blocks along hidden.
+//
+// "[FP8][MoE] Honor UE8M0 activation scales in Triton MoE" (Motivation, "More
+// context"): the activations entering each expert linear layer are quantized
+// to FP8 with FP32 block scales; the checkpoint's `scale_fmt: ue8m0` asks for
+// power-of-two scales where the older path used the continuous amax / 448.
+// Both policies are here (the second for comparison):
+//  * power-of-two: e = least integer with amax <= 448 * 2^e, byte e + 127,
+//    q = e4m3(x / 2^e) -- the same device code as the finalize epilogue;
+//  * continuous: s = amax / 448 (one correctly rounded fp32 division; 1 for
+//    an all-zero block), q = e4m3(x / s) (fp32 division, then the plain E4M3
+//    converter, nearest even), the scale stored as float32.
+//
+// One wavefront per (token, 512 columns): each lane loads 8 bf16 (16 bytes),
+// a 1 x 128 block is one 16-lane DPP row. HBM-bound: 2 bytes read and 1 byte
+// written per element, plus the scales.
+
+#include "device_common.h"
+#include "moef_internal.h"
+
+namespace moef {
+namespace {
+
+using namespace dev;
+
+template <bool POW2>
+__global__ void __launch_bounds__(kWavesPerBlock * kWaveLanes)
+act_quant_kernel(const u32x4* __restrict__ x, int tokens, int h8, int nchunks,
+                 u32x2* __restrict__ out_q, uint8_t* __restrict__ scale_e8m0,
+                 float* __restrict__ scale_f32) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int unit = (int)blockIdx.x * kWavesPerBlock + wave;
+  if ((int64_t)unit >= (int64_t)tokens * nchunks) return;      // whole waves
+  const int t = unit / nchunks;
+  const int colv = (unit - t * nchunks) * kWaveLanes + lane;
+  const bool active = colv < h8;                                // h8 % 16 == 0
+  const int64_t col = active ? colv : h8 - 1;
+
+  const u32x4 v = __builtin_nontemporal_load(x + (int64_t)t * h8 + col);
+  const uint32_t amax = row16_max(active ? absmax8_bits(v) : 0u);
+  u32x2 q;
+  if (POW2) {
+    const int ex = ue8m0_exponent(amax);
+    q = e4m3x8_scaled(v, ue8m0_scale(ex));
+    if (active && (lane & 15) == 0)
+      scale_e8m0[(int64_t)t * (h8 >> 4) + (colv >> 4)] = (uint8_t)(ex + 127);
+  } else {
+    const float a = __uint_as_float(amax << 16);
+    const float s = a > 0.0f ? a / 448.0f : 1.0f;
+    float f[8];
+    unpack8(v, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = f[e] / s;
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+    q = u32x2{(uint32_t)lo, (uint32_t)hi};
+    if (active && (lane & 15) == 0) scale_f32[(int64_t)t * (h8 >> 4) + (colv >> 4)] = s;
+  }
+  if (active) __builtin_nontemporal_store(q, out_q + (int64_t)t * h8 + colv);
+}
+
+}  // namespace
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t tokens, int64_t hidden, uint8_t* out_q,
+                            uint8_t* scale_e8m0, float* scale_f32, hipStream_t stream) {
+  const int h8 = (int)(hidden / kVecElems);
+  const int nchunks = (h8 + kWaveLanes - 1) / kWaveLanes;
+  const int64_t units = tokens * nchunks;
+  const dim3 grid((unsigned int)((units + kWavesPerBlock - 1) / kWavesPerBlock));
+  const dim3 block(kWavesPerBlock * kWaveLanes);
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  u32x2* q = reinterpret_cast<u32x2*>(out_q);
+  if (scale_e8m0 != nullptr)
+    hipLaunchKernelGGL(act_quant_kernel<true>, grid, block, 0, stream, xv, (int)tokens, h8,
+                       nchunks, q, scale_e8m0, scale_f32);
+  else
+    hipLaunchKernelGGL(act_quant_kernel<false>, grid, block, 0, stream, xv, (int)tokens, h8,
+                       nchunks, q, scale_e8m0, scale_f32);
+  return hipGetLastError();
+}
+
+}  // namespace moef

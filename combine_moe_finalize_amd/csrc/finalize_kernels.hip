@@ -36,17 +36,14 @@
 //    ("[FP8][MoE] Honor UE8M0 activation scales in Triton MoE", Motivation
 //    and "More context".)
 
+#include "device_common.h"
 #include "moef_internal.h"
 
 namespace moef {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x2 __attribute__((ext_vector_type(2)));
+using namespace dev;
+
 
 // Kernel-side view of one routed call.
 struct GatherArgs {
@@ -64,33 +61,7 @@ struct GatherArgs {
   int32_t* err;
 };
 
-// ------------------------------------------------------------ bf16 helpers
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// Two fp32 values -> one word of two bf16 (lo in bits 0..15), round to nearest
-// even, by gfx950's packed converter (NaN stays a quiet NaN with its sign).
-__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
-}
-
-__device__ __forceinline__ void unpack8(const u32x4 v, float x[8]) {
-  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
-  x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
-  x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
-}
-
-// Eight fp32 values -> eight bf16 in one 16-byte vector (one rounding each).
-__device__ __forceinline__ u32x4 pack8_rne(const float x[8]) {
-  u32x4 v;
-  v.x = bf16x2_rne(x[0], x[1]);
-  v.y = bf16x2_rne(x[2], x[3]);
-  v.z = bf16x2_rne(x[4], x[5]);
-  v.w = bf16x2_rne(x[6], x[7]);
-  return v;
-}
+// (bf16 / E4M3 conversion and packing helpers: device_common.h)
 
 // ------------------------------------------------------------- gather core
 
@@ -204,12 +175,6 @@ finalize_kernel(GatherArgs a, u32x4* __restrict__ out) {
 
 // ------------------------------------------------------- residual + RMSNorm
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
-}
-
 template <int KMAX, bool EXACT, int CPT>
 __global__ void __launch_bounds__(kNormMaxThreads)
 finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __restrict__ gamma,
@@ -275,57 +240,6 @@ finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __rest
 }
 
 // ------------------------------------------------------- UE8M0 / E4M3 quant
-
-// Largest value across the 16 lanes of a DPP row (every lane gets it).
-__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));   // row_ror:8
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));   // row_ror:4
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x122, 0xF, 0xF, false));   // row_ror:2
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x121, 0xF, 0xF, false));   // row_ror:1
-  return v;
-}
-
-// Largest |y| of the eight bf16 values in v, as bf16 bits: with the sign
-// cleared, bf16 bit patterns order like their magnitudes (NaN above inf).
-__device__ __forceinline__ uint32_t absmax8_bits(const u32x4 v) {
-  const u16x2 a = __builtin_elementwise_max(__builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu),
-                                            __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu));
-  const u16x2 b = __builtin_elementwise_max(__builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu),
-                                            __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu));
-  const u16x2 m = __builtin_elementwise_max(a, b);
-  return m.x > m.y ? m.x : m.y;
-}
-
-// Least e with amax <= 448 * 2^e, clamped to [-127, 127], from the bf16 bits
-// of amax >= 0. With amax = 2^E * 1.f and 448 = 2^8 * 1.75: e = E - 8, plus one
-// when 1.f > 1.75 (7-bit fraction above 0x60). Zero and subnormal amax clamp to
-// -127 (every subnormal is below 448 * 2^-127); inf / NaN give 127.
-__device__ __forceinline__ int ue8m0_exponent(uint32_t amax_bf16) {
-  const int ef = (int)(amax_bf16 >> 7);
-  if (ef == 0) return -127;
-  if (ef >= 255) return 127;
-  const int e = ef - 135 + ((amax_bf16 & 0x7Fu) > 0x60u ? 1 : 0);
-  return e < -127 ? -127 : e;
-}
-
-// 2^e as an fp32 scale operand; 2^-127 is the subnormal 0x00400000.
-__device__ __forceinline__ float ue8m0_scale(int e) {
-  return __uint_as_float(e > -127 ? (uint32_t)(e + 127) << 23 : 0x00400000u);
-}
-
-// Eight bf16 values y -> eight OCP E4M3 codes of y / 2^e (round to nearest
-// even, subnormals and the sign of zero kept, beyond 448 / NaN -> NaN code),
-// two per gfx950 scaled fp32 converter op, in column order. (The scale only
-// ever is an exact power of two, so the division is exact.)
-__device__ __forceinline__ u32x2 e4m3x8_scaled(const u32x4 y, float scale) {
-  float f[8];
-  unpack8(y, f);
-  s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((s16x2){0, 0}, f[0], f[1], scale, false);
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, f[2], f[3], scale, true);
-  s16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((s16x2){0, 0}, f[4], f[5], scale, false);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, f[6], f[7], scale, true);
-  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-}
 
 template <int KMAX, bool EXACT>
 __global__ void __launch_bounds__(kWavesPerBlock * kWaveLanes)

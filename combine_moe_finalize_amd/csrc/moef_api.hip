@@ -98,6 +98,30 @@ bool overlaps_any(const void* p, int64_t n, const Span* s, int ns) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOEF_OK : MOEF_ERR_HIP; }
 
+// Shared checks and launch of the two activation-quant entry points.
+int act_quant(const uint16_t* x, int64_t num_tokens, int64_t hidden, uint8_t* out_e4m3,
+              uint8_t* scale_e8m0, float* scale_f32, void* stream) {
+  if (num_tokens < 0 || hidden < 1) return MOEF_ERR_BAD_SHAPE;
+  if (hidden % MOEF_QUANT_BLOCK != 0 || hidden > MOEF_MAX_HIDDEN || num_tokens > INT32_MAX)
+    return MOEF_ERR_UNSUPPORTED;
+  const int64_t nchunks = (hidden / moef::kVecElems + moef::kWaveLanes - 1) / moef::kWaveLanes;
+  if (num_tokens * nchunks > moef::kMaxUnits) return MOEF_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOEF_OK;
+  if (x == nullptr || out_e4m3 == nullptr || (scale_e8m0 == nullptr && scale_f32 == nullptr))
+    return MOEF_ERR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(out_e4m3, 8) || !aligned(scale_f32, 4))
+    return MOEF_ERR_MISALIGNED;
+  const int64_t xb = num_tokens * hidden * 2;
+  const int64_t qb = num_tokens * hidden;
+  const int64_t sb = num_tokens * (hidden / MOEF_QUANT_BLOCK) * (scale_f32 != nullptr ? 4 : 1);
+  const void* sp = scale_f32 != nullptr ? (const void*)scale_f32 : (const void*)scale_e8m0;
+  if (overlap(out_e4m3, qb, x, xb) || overlap(sp, sb, x, xb) || overlap(out_e4m3, qb, sp, sb))
+    return MOEF_ERR_BAD_ALIAS;
+  return hip_status(moef::launch_act_quant(x, num_tokens, hidden, out_e4m3, scale_e8m0,
+                                           scale_f32, static_cast<hipStream_t>(stream)));
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -248,6 +272,18 @@ int moe_topk_sigmoid_gate(const float* router_logits, int64_t num_tokens, int32_
   return hip_status(moef::launch_topk_sigmoid_gate(router_logits, num_tokens, num_experts,
                                                    top_k, topk_ids, topk_weights, topk_packed,
                                                    static_cast<hipStream_t>(stream)));
+}
+
+int moe_act_quant_fp8_ue8m0(const uint16_t* x, int64_t num_tokens, int64_t hidden,
+                            uint8_t* out_e4m3, uint8_t* scale_e8m0, void* stream) {
+  if (scale_e8m0 == nullptr && num_tokens > 0) return MOEF_ERR_NULL_POINTER;
+  return act_quant(x, num_tokens, hidden, out_e4m3, scale_e8m0, nullptr, stream);
+}
+
+int moe_act_quant_fp8_amax(const uint16_t* x, int64_t num_tokens, int64_t hidden,
+                           uint8_t* out_e4m3, float* scale_f32, void* stream) {
+  if (scale_f32 == nullptr && num_tokens > 0) return MOEF_ERR_NULL_POINTER;
+  return act_quant(x, num_tokens, hidden, out_e4m3, nullptr, scale_f32, stream);
 }
 
 }  // extern "C"

@@ -40,6 +40,10 @@ hipError_t launch_packed_decode(const int32_t* packed, int64_t n,
                                 int32_t* expert_ids, float* weights,
                                 hipStream_t stream);
 
+// exactly one of scale_e8m0 (power-of-two policy) / scale_f32 (amax / 448)
+hipError_t launch_act_quant(const uint16_t* x, int64_t tokens, int64_t hidden, uint8_t* out_q,
+                            uint8_t* scale_e8m0, float* scale_f32, hipStream_t stream);
+
 hipError_t launch_topk_sigmoid_gate(const float* logits, int64_t tokens, int32_t experts,
                                     int32_t top_k, int32_t* ids, float* weights,
                                     int32_t* packed, hipStream_t stream);

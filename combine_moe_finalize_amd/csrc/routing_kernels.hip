@@ -19,13 +19,13 @@
 // memory traffic. Lane r keeps round r's winner. Lanes 0..top_k-1 then
 // evaluate their sigmoid, the wave sums them, and each writes its slot.
 
+#include "device_common.h"
 #include "moef_internal.h"
 
 namespace moef {
 namespace {
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+using namespace dev;
 
 constexpr int kGateWaves = 4;
 
@@ -133,8 +133,7 @@ topk_sigmoid_gate_kernel(const float* __restrict__ logits, int tokens, int exper
     ids[o] = my_id;
     if (weights != nullptr) weights[o] = w;
     if (packed != nullptr) {
-      const uint32_t wb =
-          __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){w, 0.0f}, bf16x2)) & 0xFFFFu;
+      const uint32_t wb = bf16x2_rne(w, 0.0f) & 0xFFFFu;
       packed[o] = (int32_t)(((uint32_t)my_id << 16) | wb);
     }
   }

@@ -185,6 +185,16 @@ def router_logits(T: int, E: int, seed: int, scale: float = 1.0) -> np.ndarray:
     return (g.standard_normal((T, E), dtype=np.float32) * np.float32(scale))
 
 
+def activations(T: int, H: int, seed: int, log2_mag: Optional[tuple] = (-8.0, 8.0)) -> np.ndarray:
+    """bf16 activations [T, H]: bf16(m_t * N(0,1)) with a per-token magnitude
+    m_t = 2^U(lo, hi) (or 1 when log2_mag is None)."""
+    scale = None
+    if log2_mag is not None:
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 6])))
+        scale = np.exp2(g.uniform(log2_mag[0], log2_mag[1], size=T)).astype(np.float32)
+    return _bf16_normal_matrix(seed, 7, T, H, scale)
+
+
 # The five synthetic workload families (sizes as in the published setup).
 CONFIGS = {
     0: dict(name="tiny", Ts=(1,), H=1024, E=16, top_k=2),

@@ -206,6 +206,31 @@ int moe_topk_sigmoid_gate(const float* router_logits, int64_t num_tokens,
                           int32_t* topk_ids, float* topk_weights, int32_t* topk_packed,
                           void* stream);
 
+/*
+ * moe_act_quant_fp8_ue8m0 / moe_act_quant_fp8_amax - standalone FP8 E4M3
+ * activation quantization with one FP32 scale per 1 x 128 block along hidden,
+ * for the activations entering the expert linear layers ("[FP8][MoE] Honor
+ * UE8M0 activation scales in Triton MoE", Motivation and "More context").
+ *
+ *  x           bf16 [num_tokens, hidden], finite values (a NaN or inf makes
+ *              its block's codes unspecified).
+ *  hidden      a multiple of 128.
+ *  out_e4m3    uint8 [num_tokens, hidden], OCP E4M3 codes.
+ *  _ue8m0:     power-of-two scales, the finalize epilogue's rule:
+ *              scale_e8m0 uint8 [num_tokens, hidden / 128] = e + 127, e the
+ *              least integer with max|x| <= 448 * 2^e (clamped to [-127, 127]),
+ *              codes = e4m3(x / 2^e).
+ *  _amax:      the continuous policy the pages replace, for comparison:
+ *              scale_f32 float32 [num_tokens, hidden / 128] = max|x| / 448
+ *              (correctly rounded fp32; 1 for an all-zero block),
+ *              codes = e4m3(fp32(x / scale)), nearest even.
+ *  num_tokens == 0 is a no-op.
+ */
+int moe_act_quant_fp8_ue8m0(const uint16_t* x, int64_t num_tokens, int64_t hidden,
+                            uint8_t* out_e4m3, uint8_t* scale_e8m0, void* stream);
+int moe_act_quant_fp8_amax(const uint16_t* x, int64_t num_tokens, int64_t hidden,
+                           uint8_t* out_e4m3, float* scale_f32, void* stream);
+
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* moe_finalize_status_string(int status);
 

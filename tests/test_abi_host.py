@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"moe_finalize", "moe_finalize_residual_rmsnorm",
                           "moe_finalize_quant_ue8m0", "moe_topk_packed_decode",
                           "moe_finalize_status_string", "moe_finalize_abi_version",
-                          "moe_topk_sigmoid_gate"}
+                          "moe_topk_sigmoid_gate", "moe_act_quant_fp8_ue8m0",
+                          "moe_act_quant_fp8_amax"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -177,3 +178,20 @@ def test_gate_rules(lib):
     assert g(LG + 2, 4, 256, 8, ID, WT, PKD, None) == MISAL
     assert g(LG, 4, 256, 8, LG + 64, WT, PKD, None) == ALIAS   # ids inside the logits
     assert g(LG, 4, 256, 8, ID, ID + 16, PKD, None) == ALIAS   # weights overlap ids
+
+
+def test_act_quant_rules(lib):
+    for fn in (lib.moe_act_quant_fp8_ue8m0, lib.moe_act_quant_fp8_amax):
+        X, QQ, SS = G2, Q, S
+        assert fn(X, -1, 7168, QQ, SS, None) == SHAPE
+        assert fn(X, 4, 0, QQ, SS, None) == SHAPE
+        assert fn(X, 4, 7168 + 8, QQ, SS, None) == UNSUP          # not a multiple of 128
+        assert fn(X, 0, 7168, None, None, None) == OK
+        assert fn(None, 4, 7168, QQ, SS, None) == NULLP
+        assert fn(X, 4, 7168, None, SS, None) == NULLP
+        assert fn(X, 4, 7168, QQ, None, None) == NULLP
+        assert fn(X + 8, 4, 7168, QQ, SS, None) == MISAL
+        assert fn(X, 4, 7168, QQ + 4, SS, None) == MISAL
+        assert fn(X, 4, 7168, X + 64, SS, None) == ALIAS           # codes inside x
+        assert fn(X, 4, 7168, QQ, QQ + 100, None) == ALIAS         # scales inside codes
+    assert lib.moe_act_quant_fp8_amax(G2, 4, 7168, Q, S + 2, None) == MISAL
