@@ -23,8 +23,9 @@ Printed: one JSON line with
   sweep      microseconds per call and GB/s for the other workload shapes
              (decode T=1..256, packed vs fp32 routing, residual + RMSNorm,
              packed decode, the routing gate, standalone FP8 activation
-             quant in both scale policies; for the gate the "H" field holds
-             the expert count E): per-call HIP-event times (which include a few
+             quant in both scale policies, the expert-parallel combine of
+             four partials; for the gate the "H" field holds the expert
+             count E): per-call HIP-event times (which include a few
              microseconds of event overhead), warm and cold (after streaming
              a 1 GiB buffer through the caches); the sustained per-call time
              of 100 back-to-back calls; and the per-call time of 20 calls
@@ -267,6 +268,15 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
                 lambda: M.moe_act_quant_fp8_ue8m0(xa, out_e4m3=aq, scale_e8m0=a8), iters_small)
         measure("act_quant_amax", T, H, 0, T * (3 * H + 4 * (H // 128)),
                 lambda: M.moe_act_quant_fp8_amax(xa, out_e4m3=aq, scale_f32=af), iters_small)
+    T, H, R = 8192, 7168, 4
+    parts = torch.from_numpy(W.activations(R * T, H, seed=R, log2_mag=None).view(np.int16)).view(
+        torch.bfloat16).to("cuda:0").view(R, T, H)
+    shp = torch.from_numpy(W.activations(T, H, seed=5, log2_mag=None).view(np.int16)).view(
+        torch.bfloat16).to("cuda:0")
+    ep_out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda:0")
+    measure("ep_combine_R4", T, H, 0, T * H * 2 * (R + 2),
+            lambda: M.moe_finalize_ep_combine(parts, shared_out=shp, out=ep_out), iters_big)
+    del parts, shp, ep_out
     n = 8192 * 8
     pk = torch.from_numpy(W.config_workload(0).packed.reshape(-1).repeat(n // 2)).to("cuda:0")
     ids = torch.empty_like(pk)

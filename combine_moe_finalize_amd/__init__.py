@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     moe_act_quant_fp8_amax,
     moe_act_quant_fp8_ue8m0,
     moe_finalize,
+    moe_finalize_ep_combine,
     moe_finalize_quant_ue8m0,
     moe_finalize_residual_rmsnorm,
     moe_topk_packed_decode,

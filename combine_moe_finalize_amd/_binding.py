@@ -48,6 +48,7 @@ _SIGNATURES = {
     "moe_topk_sigmoid_gate": [c_void_p, c_i64, c_i32, c_i32, c_void_p, c_void_p, c_void_p,
                               c_void_p],
     "moe_act_quant_fp8_ue8m0": [c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_void_p],
+    "moe_finalize_ep_combine": [c_void_p, c_i32, c_void_p, c_void_p, c_i64, c_i64, c_void_p],
     "moe_act_quant_fp8_amax": [c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_void_p],
     "moe_finalize_status_string": [ctypes.c_int],
     "moe_finalize_abi_version": [],
@@ -328,3 +329,24 @@ def moe_act_quant_fp8_amax(x: torch.Tensor, *, out_e4m3: Optional[torch.Tensor] 
                            scale_f32: Optional[torch.Tensor] = None):
     """(codes uint8 [T, H], scales float32 [T, H/128]): s = amax / 448."""
     return _act_quant("moe_act_quant_fp8_amax", x, out_e4m3, scale_f32, torch.float32)
+
+
+def moe_finalize_ep_combine(partials: torch.Tensor, *,
+                            shared_out: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [T, H] = sum of the R expert-parallel partials [R, T, H] (+ shared)."""
+    if not isinstance(partials, torch.Tensor) or partials.dim() != 3:
+        raise ValueError("partials must be a 3-D [ranks, tokens, hidden] tensor")
+    R, T, H = partials.shape
+    device = partials.device
+    _tensor(partials, "partials", torch.bfloat16, (R, T, H))
+    if shared_out is not None:
+        _tensor(shared_out, "shared_out", torch.bfloat16, (T, H))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    _tensor(out, "out", torch.bfloat16, (T, H))
+    _on_device(device, partials=partials, shared_out=shared_out, out=out)
+    st = load_library().moe_finalize_ep_combine(_ptr(partials), R, _ptr(shared_out), _ptr(out),
+                                                T, H, _stream(device))
+    _check("moe_finalize_ep_combine", st)
+    return out

@@ -285,6 +285,48 @@ packed_decode_kernel(const uint32_t* __restrict__ packed, int64_t n,
   if (w != nullptr) w[i] = __uint_as_float(word << 16);
 }
 
+// ------------------------------------------------- expert-parallel combine
+
+// out = bf16(sum_r partial_r + shared): with experts sharded over R ranks,
+// each rank finalizes only its own slots (the others carry index -1) and no
+// shared output; the shared expert is added once, here. fp32 adds in rank
+// order, one rounding. Loads are issued four ranks at a time.
+__global__ void __launch_bounds__(256)
+ep_combine_kernel(const u32x4* __restrict__ partials, int R, int64_t stride,
+                  const u32x4* __restrict__ shared, u32x4* __restrict__ out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  int r = 0;
+  for (; r + 4 <= R; r += 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(partials + (r + j) * stride + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float x[8];
+      unpack8(v[j], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + x[e];
+    }
+  }
+  for (; r < R; ++r) {
+    float x[8];
+    unpack8(__builtin_nontemporal_load(partials + r * stride + i), x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + x[e];
+  }
+  if (shared != nullptr) {
+    float x[8];
+    unpack8(__builtin_nontemporal_load(shared + i), x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + x[e];
+  }
+  __builtin_nontemporal_store(pack8_rne(acc), out + i);
+}
+
 // ---------------------------------------------------------------- dispatch
 
 template <int V>
@@ -379,6 +421,17 @@ hipError_t launch_finalize_quant(const Routed& r, uint8_t* out_e4m3, uint8_t* sc
                        dim3(kWavesPerBlock * kWaveLanes), 0, stream, a, q, scale_e8m0);
     return hipGetLastError();
   });
+}
+
+hipError_t launch_ep_combine(const uint16_t* partials, int32_t num_partials,
+                             const uint16_t* shared, uint16_t* out, int64_t tokens,
+                             int64_t hidden, hipStream_t stream) {
+  const int64_t n = tokens * (hidden / kVecElems);
+  const unsigned int blocks = (unsigned int)((n + 255) / 256);
+  hipLaunchKernelGGL(ep_combine_kernel, dim3(blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(partials), (int)num_partials, n,
+                     reinterpret_cast<const u32x4*>(shared), reinterpret_cast<u32x4*>(out), n);
+  return hipGetLastError();
 }
 
 hipError_t launch_packed_decode(const int32_t* packed, int64_t n, int32_t* expert_ids,

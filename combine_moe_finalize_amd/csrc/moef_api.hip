@@ -232,6 +232,24 @@ int moe_finalize_quant_ue8m0(const uint16_t* gemm2_out, int64_t num_rows,
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int moe_finalize_ep_combine(const uint16_t* partials, int32_t num_partials,
+                            const uint16_t* shared_out, uint16_t* out, int64_t num_tokens,
+                            int64_t hidden, void* stream) {
+  if (num_tokens < 0 || hidden < 1 || num_partials < 1 || num_partials > MOEF_MAX_EP_PARTIALS)
+    return MOEF_ERR_BAD_SHAPE;
+  if (hidden % moef::kVecElems != 0 || hidden > MOEF_MAX_HIDDEN) return MOEF_ERR_UNSUPPORTED;
+  if (num_tokens * (hidden / moef::kVecElems) > moef::kMaxUnits * 256) return MOEF_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOEF_OK;
+  if (partials == nullptr || out == nullptr) return MOEF_ERR_NULL_POINTER;
+  if (!aligned(partials, 16) || !aligned(shared_out, 16) || !aligned(out, 16))
+    return MOEF_ERR_MISALIGNED;
+  const int64_t tb = num_tokens * hidden * 2;
+  if (overlap(out, tb, partials, tb * num_partials) || overlap(out, tb, shared_out, tb))
+    return MOEF_ERR_BAD_ALIAS;
+  return hip_status(moef::launch_ep_combine(partials, num_partials, shared_out, out, num_tokens,
+                                            hidden, static_cast<hipStream_t>(stream)));
+}
+
 int moe_topk_packed_decode(const int32_t* packed, int64_t n, int32_t* expert_ids,
                            float* weights, void* stream) {
   if (n < 0) return MOEF_ERR_BAD_SHAPE;

@@ -36,6 +36,10 @@ hipError_t launch_finalize_rmsnorm(const Routed& r, const uint16_t* residual,
 hipError_t launch_finalize_quant(const Routed& r, uint8_t* out_e4m3,
                                  uint8_t* scale_e8m0, hipStream_t stream);
 
+hipError_t launch_ep_combine(const uint16_t* partials, int32_t num_partials,
+                             const uint16_t* shared, uint16_t* out, int64_t tokens,
+                             int64_t hidden, hipStream_t stream);
+
 hipError_t launch_packed_decode(const int32_t* packed, int64_t n,
                                 int32_t* expert_ids, float* weights,
                                 hipStream_t stream);

@@ -79,6 +79,7 @@ extern "C" {
 #define MOEF_MAX_HIDDEN_RMSNORM 16384 /* the RMSNorm epilogue keeps a row on chip */
 #define MOEF_QUANT_BLOCK 128         /* the UE8M0 epilogue needs hidden % 128 == 0 */
 #define MOEF_MAX_GATE_EXPERTS 512    /* the gate keeps a token's logits in registers */
+#define MOEF_MAX_EP_PARTIALS 64      /* partials one combine call may sum */
 
 #define MOEF_DEVERR_INDEX_OUT_OF_RANGE 1
 
@@ -167,6 +168,28 @@ int moe_finalize_quant_ue8m0(const uint16_t* gemm2_out, int64_t num_rows,
                              uint8_t* out_e4m3, uint8_t* scale_e8m0,
                              int64_t num_tokens, int64_t hidden, int32_t top_k,
                              int32_t* err_flag, void* stream);
+
+/*
+ * moe_finalize_ep_combine - sum of expert-parallel finalize partials.
+ * The finalize is linear, so with the experts sharded over R ranks each rank
+ * can run moe_finalize on its own slots only (every other slot's index set to
+ * -1, which the finalize skips) and without the shared-expert output; this
+ * call adds the R partials and the shared output, once. ("[Deepseek V4] Keep
+ * fp32 routing weights in the mxfp4 trtllm MoE", follow-up commit: a TP4 /
+ * EP4 deployment; "[Kimi K2.5] Fuse deferred MoE finalize into next-layer AR
+ * + residual + RMSNorm", "Numerics & speed": the cross-rank reduction runs
+ * over the finalized rows.) On one GPU the partials arrive in one buffer.
+ *
+ *  partials     bf16 [num_partials, num_tokens, hidden], rank-major.
+ *  num_partials R in [1, MOEF_MAX_EP_PARTIALS].
+ *  shared_out   bf16 [num_tokens, hidden] or NULL.
+ *  out          bf16 [num_tokens, hidden] = bf16(+0 + p_0 + ... + p_{R-1}
+ *               [+ shared]), fp32 adds in rank order, one rounding.
+ *  hidden       a multiple of 8. num_tokens == 0 is a no-op.
+ */
+int moe_finalize_ep_combine(const uint16_t* partials, int32_t num_partials,
+                            const uint16_t* shared_out, uint16_t* out,
+                            int64_t num_tokens, int64_t hidden, void* stream);
 
 /*
  * moe_topk_packed_decode - split packed routing words.

@@ -236,3 +236,43 @@ def finalize_quant_mirror(gemm2_out, idx, weights_f32=None, packed=None,
     y, flag = finalize_mirror(gemm2_out, idx, weights_f32, packed, shared, rsf)
     codes, scales, _ = quant_ue8m0(y)
     return codes, scales, flag
+
+
+# ------------------------------------------------- expert-parallel partials
+
+def ep_rank_slots(expert_ids, num_experts, num_ranks, rank):
+    """Which slots a rank holds when experts are split into num_ranks
+    contiguous, equal ranges (reading: EP shards the expert dimension)."""
+    per = -(-num_experts // num_ranks)
+    e = np.asarray(expert_ids)
+    return (e >= rank * per) & (e < (rank + 1) * per)
+
+
+def ep_partial_index(idx, expert_ids, num_experts, num_ranks, rank, row_offset=0):
+    """The rank-local index map: a held slot's row minus the rank's first row
+    (its local gemm2_out starts there), -1 for every other slot (skipped)."""
+    held = ep_rank_slots(expert_ids, num_experts, num_ranks, rank)
+    return np.where(held, np.asarray(idx, np.int64) - row_offset, -1).astype(np.int32)
+
+
+def ep_combine_mirror(partials, shared=None):
+    """Combine of bf16 partials [R, T, H] (readings: the finalize is linear, so
+    each rank finalizes its own slots; the shared-expert output is added once,
+    here): acc = +0; acc = acc + partial_r for r ascending; acc = acc + shared;
+    one rounding to bf16. fp32 steps, as the combine kernel does them."""
+    p = np.asarray(partials, dtype=np.uint16)
+    acc = np.zeros(p.shape[1:], dtype=np.float32)
+    for r in range(p.shape[0]):
+        acc = acc + F.bf16_to_f32(p[r])
+    if shared is not None:
+        acc = acc + F.bf16_to_f32(shared)
+    return F.bf16_bits(acc)
+
+
+def ep_combine_truth(partials, shared=None):
+    """Same, with the sum in float64 (one rounding)."""
+    p = np.asarray(partials, dtype=np.uint16)
+    acc = F.bf16_to_f64(p).sum(axis=0)
+    if shared is not None:
+        acc = acc + F.bf16_to_f64(shared)
+    return F.bf16_bits(acc)

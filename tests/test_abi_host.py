@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
                           "moe_finalize_quant_ue8m0", "moe_topk_packed_decode",
                           "moe_finalize_status_string", "moe_finalize_abi_version",
                           "moe_topk_sigmoid_gate", "moe_act_quant_fp8_ue8m0",
-                          "moe_act_quant_fp8_amax"}
+                          "moe_act_quant_fp8_amax", "moe_finalize_ep_combine"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -195,3 +195,18 @@ def test_act_quant_rules(lib):
         assert fn(X, 4, 7168, X + 64, SS, None) == ALIAS           # codes inside x
         assert fn(X, 4, 7168, QQ, QQ + 100, None) == ALIAS         # scales inside codes
     assert lib.moe_act_quant_fp8_amax(G2, 4, 7168, Q, S + 2, None) == MISAL
+
+
+def test_ep_combine_rules(lib):
+    c = lib.moe_finalize_ep_combine
+    PP = G2
+    assert c(PP, 0, SH, OUT, 4, 4096, None) == SHAPE
+    assert c(PP, 65, SH, OUT, 4, 4096, None) == SHAPE
+    assert c(PP, 4, SH, OUT, -1, 4096, None) == SHAPE
+    assert c(PP, 4, SH, OUT, 4, 4100, None) == UNSUP
+    assert c(PP, 4, SH, OUT, 0, 4096, None) == OK
+    assert c(None, 4, SH, OUT, 4, 4096, None) == NULLP
+    assert c(PP, 4, SH, None, 4, 4096, None) == NULLP
+    assert c(PP + 8, 4, SH, OUT, 4, 4096, None) == MISAL
+    assert c(PP, 4, SH, PP + 3 * 4 * 4096 * 2, 4, 4096, None) == ALIAS   # out = last partial
+    assert c(PP, 4, SH, SH, 4, 4096, None) == ALIAS
