@@ -56,5 +56,26 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+C_DRIVER_SRC = os.path.join(os.path.dirname(os.path.dirname(LIB_DIR)), "tests", "c",
+                            "abi_driver.c")
+C_DRIVER = os.path.splitext(C_DRIVER_SRC)[0]
+
+
+def build_c_driver() -> str:
+    """Compile the plain-C ABI driver used by the tests (gcc, links the library
+    and the HIP runtime; the library is found through a relative rpath)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", os.path.join(rocm, "include"), C_DRIVER_SRC,
+           "-L", LIB_DIR, "-lmoe_finalize", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../combine_moe_finalize_amd/_lib",
+           "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", C_DRIVER]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    return C_DRIVER
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_driver())

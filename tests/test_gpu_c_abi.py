@@ -1,0 +1,52 @@
+"""The C ABI from plain C: a gcc-built driver (tests/c/abi_driver.c) links the
+library and the HIP runtime, with no Python or torch, runs the finalize (fp32
+and packed weights) and the UE8M0 quant on a stream it creates, and checks
+rejected calls; its outputs are compared here with the CPU oracle."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+from combine_moe_finalize_amd import workloads as W
+from oracle import finalize as O
+
+from gpu_helpers import announce, assert_bits_equal
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DRIVER = os.path.join(ROOT, "tests", "c", "abi_driver")
+
+
+@pytest.mark.parametrize("T,H,E,k", [(7, 1024, 16, 2), (64, 7168, 256, 8), (5, 1000, 32, 3)])
+def test_c_driver_matches_oracle(tmp_path, T, H, E, k):
+    if not os.path.exists(DRIVER):
+        pytest.fail(f"{DRIVER} is not built (run __graft_entry__.build())")
+    wl = W.make_workload(T, H, E, k, rsf=2.5, seed=T + H)
+    d = str(tmp_path)
+    with open(os.path.join(d, "meta.txt"), "w") as f:
+        f.write(f"{wl.T} {wl.H} {wl.top_k} {wl.P} {wl.rsf}\n")
+    wl.gemm2_out.tofile(os.path.join(d, "g2.bin"))
+    wl.idx.tofile(os.path.join(d, "idx.bin"))
+    wl.weights.tofile(os.path.join(d, "w.bin"))
+    wl.packed.tofile(os.path.join(d, "packed.bin"))
+    wl.shared.tofile(os.path.join(d, "shared.bin"))
+    announce(f"C driver T={T} H={H} k={k}")
+    res = subprocess.run([DRIVER, d], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    out = np.fromfile(os.path.join(d, "out.bin"), dtype=np.uint16).reshape(T, H)
+    outp = np.fromfile(os.path.join(d, "out_packed.bin"), dtype=np.uint16).reshape(T, H)
+    ref, _ = O.finalize_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights, shared=wl.shared,
+                               rsf=wl.rsf)
+    refp, _ = O.finalize_mirror(wl.gemm2_out, wl.idx, packed=wl.packed, shared=wl.shared,
+                                rsf=wl.rsf)
+    assert_bits_equal(out, ref, "C driver fp32")
+    assert_bits_equal(outp, refp, "C driver packed")
+    assert np.fromfile(os.path.join(d, "err.bin"), dtype=np.int32)[0] == 0
+    if H % 128 == 0:
+        q = np.fromfile(os.path.join(d, "q.bin"), dtype=np.uint8).reshape(T, H)
+        s = np.fromfile(os.path.join(d, "s.bin"), dtype=np.uint8).reshape(T, H // 128)
+        mq, ms, _ = O.quant_ue8m0(ref)
+        assert_bits_equal(s, ms, "C driver scales")
+        assert_bits_equal(q, mq, "C driver codes")
