@@ -178,3 +178,32 @@ def test_odd_large_token_count():
     torch.cuda.synchronize()
     oq, os_ = A.act_quant_amax(xa)
     assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(s.cpu().numpy(), os_)
+
+
+def test_largest_row_indices():
+    """num_rows = 2^31 - 1 rows of H = 8 (32 GiB): rows near the top of the
+    int32 index range sit more than 2^34 bytes into gemm2_out, so any 32-bit
+    offset arithmetic would fail. Only the gathered rows are written; the
+    expected values come from the same rows in a compact buffer (layout
+    invariance) through the oracle."""
+    H, T, K = 8, 64, 4
+    P = 2 ** 31 - 1
+    wl = W.make_workload(T, H, 16, K, rsf=2.5, seed=12, pad=8)
+    rng = np.random.default_rng(13)
+    top = P - 1 - rng.choice(2 ** 20, size=T * K, replace=False)   # distinct rows near the top
+    idx_big = top.reshape(T, K).astype(np.int32)
+    compact = wl.gemm2_out[wl.idx.reshape(-1)]                       # the rows, in slot order
+    announce(f"largest row indices: P={P} H={H}")
+    g2 = torch.empty((P, H), dtype=torch.bfloat16, device=DEV)     # 32 GiB, not initialised
+    g2[torch.from_numpy(top).to(DEV)] = d_bf16(compact)
+    out = M.moe_finalize(g2, d_i32(idx_big), topk_weights=d_f32(wl.weights),
+                         shared_out=d_bf16(wl.shared), routed_scaling_factor=wl.rsf)
+    torch.cuda.synchronize()
+    got = h_bits(out)
+    del g2
+    torch.cuda.empty_cache()
+    idx_c = np.arange(T * K, dtype=np.int32).reshape(T, K)
+    ref, flag = O.finalize_mirror(compact, idx_c, weights_f32=wl.weights, shared=wl.shared,
+                                  rsf=wl.rsf)
+    assert flag == 0
+    assert_bits_equal(got, ref, "largest row indices")
