@@ -301,8 +301,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the finalize shards by token with no exchange; see the design notes)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the finalize "
+              f"shards by token with no exchange, so N GPUs would each run this same "
+              f"single-GPU step on T/N tokens)",
               file=sys.stderr)
         sys.exit(2)
 

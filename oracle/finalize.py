@@ -25,8 +25,7 @@ What is computed (plain definition, written from the pages):
 * Power-of-two (UE8M0) FP8 activation scales ("[FP8][MoE] Honor UE8M0
   activation scales in Triton MoE", Motivation and "More context").
 
-Readings taken where the pages are silent (each is listed with its reason in
-the design notes):
+Readings taken where the pages are silent:
   R1  out[t,h] = bf16( sum_k w'[t,k] * x[perm[t,k], h] + shared[t,h] ),
       w' = fp32(w * rsf); rsf scales routed experts only, never shared.
   R2  one rounding to bf16 (nearest-even) at the very end.
@@ -43,7 +42,7 @@ the design notes):
 Two modes:
   * ``*_truth``: fp64 gather, products and sums (each product w' * x is
     exact in fp64: 24 x 8 significand bits), one final rounding. This is
-    the contract the GPU is judged against, within tolerance.
+    the contract the GPU is checked against, within tolerance.
   * ``*_mirror``: the fp32 operation sequence the kernels are asked to
     follow, each op rounded to fp32 with no fused multiply-add:
     acc = +0; for k ascending: acc = acc + (w'_k * x_k); acc = acc + shared;

@@ -2,7 +2,7 @@
 
 This module is part of the oracle: plain, slow, obviously-correct numpy code
 that the tests, the smoke check and the benchmark's CPU-baseline leg use to
-judge the HIP library. Nothing in the product path may import it.
+check the HIP library. Nothing in the product path may import it.
 
 Every helper is written from a format definition, never from a vendor
 library, and rounds with the plain "grid" method: find the spacing of the

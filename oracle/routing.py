@@ -7,7 +7,7 @@ The pages name the step before the finalize: a gate ("moe_fused_gate")
 that produces fp32 routing weights, optionally packed by "PackTopkIds" into
 (expert_id << 16) | bf16(weight) ("[Deepseek V4] Keep fp32 routing weights
 in the mxfp4 trtllm MoE", PR description). They give no formula. Readings
-taken (listed with their reasons in the design notes):
+taken:
   G1  scores are sigmoid(logit); the top_k experts are the top_k scores,
       which, sigmoid being increasing, are the top_k logits: the integer
       decision never depends on how sigmoid is evaluated;
