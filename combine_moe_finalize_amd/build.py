@@ -76,6 +76,27 @@ def build_c_driver() -> str:
     return C_DRIVER
 
 
+HOST_CHECKS = os.path.join(os.path.dirname(C_DRIVER_SRC), "host_checks")
+
+
+def build_host_checks() -> str:
+    """Compile the C-ABI argument checks against host-only launch stubs with
+    the address and undefined-behaviour sanitizers on the host side (no GPU
+    code is built with them)."""
+    cdir = os.path.dirname(C_DRIVER_SRC)
+    sanitize = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined".split()
+    cmd = [hipcc(), "-O1", "-g", "-std=c++17", *sanitize,
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, "moef_api.hip"),
+           os.path.join(cdir, "launch_stub.cpp"), os.path.join(cdir, "host_checks.cpp"),
+           "-o", HOST_CHECKS]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stderr}")
+    return HOST_CHECKS
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_c_driver())
+    print(build_host_checks())
