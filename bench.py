@@ -390,6 +390,13 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_sweep:
         result["sweep"] = sweep(torch, M, W)
+        # us/call over T = 1..8192: decode finalize (H=4096, top_k=8) per call
+        # under HIP-graph replay, and the timed prefill launch (T=8192)
+        per_call = {str(r["T"]): r["us_graph_replay"] for r in result["sweep"]
+                    if r["case"] == "decode"}
+        per_call["8192"] = round(avg_us, 3)
+        result["us_per_call"] = {"decode_finalize_H4096_k8_graph_replay_and_prefill_T8192":
+                                 per_call}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(wl)
