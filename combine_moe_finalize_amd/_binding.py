@@ -161,6 +161,14 @@ def _check(fn, status):
         raise MoeFinalizeError(fn, status)
 
 
+def _call(name, device, *args):
+    """Call the C entry point with the tensors' device current (kernels launch
+    on the current device; the stream passed is that device's current one)."""
+    with torch.cuda.device(device):
+        st = getattr(load_library(), name)(*args, _stream(device))
+    _check(name, st)
+
+
 # ------------------------------------------------------------- entry points
 
 def moe_finalize(gemm2_out: torch.Tensor, expanded_idx_to_permuted_idx: torch.Tensor, *,
@@ -176,9 +184,8 @@ def moe_finalize(gemm2_out: torch.Tensor, expanded_idx_to_permuted_idx: torch.Te
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
     _dev_tensor(out, "out", torch.bfloat16, (T, H), device)
-    st = load_library().moe_finalize(*args, float(routed_scaling_factor), _ptr(out), T, H, K,
-                                     _ptr(err_flag), _stream(device))
-    _check("moe_finalize", st)
+    _call("moe_finalize", device, *args, float(routed_scaling_factor), _ptr(out), T, H, K,
+          _ptr(err_flag))
     return out
 
 
@@ -205,10 +212,9 @@ def moe_finalize_residual_rmsnorm(gemm2_out: torch.Tensor,
         normed = torch.empty((T, H), dtype=torch.bfloat16, device=device)
     _dev_tensor(residual_out, "residual_out", torch.bfloat16, (T, H), device)
     _dev_tensor(normed, "normed", torch.bfloat16, (T, H), device)
-    st = load_library().moe_finalize_residual_rmsnorm(
-        *args, float(routed_scaling_factor), _ptr(residual), _ptr(gamma), float(eps),
-        _ptr(residual_out), _ptr(normed), T, H, K, _ptr(err_flag), _stream(device))
-    _check("moe_finalize_residual_rmsnorm", st)
+    _call("moe_finalize_residual_rmsnorm", device, *args, float(routed_scaling_factor),
+          _ptr(residual), _ptr(gamma), float(eps), _ptr(residual_out), _ptr(normed), T, H, K,
+          _ptr(err_flag))
     return residual_out, normed
 
 
@@ -234,10 +240,8 @@ def moe_finalize_quant_ue8m0(gemm2_out: torch.Tensor,
         out_e4m3 = out_e4m3.view(torch.uint8)
     _dev_tensor(out_e4m3, "out_e4m3", torch.uint8, (T, H), device)
     _dev_tensor(scale_e8m0, "scale_e8m0", torch.uint8, (T, H // QUANT_BLOCK), device)
-    st = load_library().moe_finalize_quant_ue8m0(
-        *args, float(routed_scaling_factor), _ptr(out_e4m3), _ptr(scale_e8m0), T, H, K,
-        _ptr(err_flag), _stream(device))
-    _check("moe_finalize_quant_ue8m0", st)
+    _call("moe_finalize_quant_ue8m0", device, *args, float(routed_scaling_factor),
+          _ptr(out_e4m3), _ptr(scale_e8m0), T, H, K, _ptr(err_flag))
     return out_e4m3, scale_e8m0
 
 
@@ -256,10 +260,8 @@ def moe_topk_packed_decode(topk_packed: torch.Tensor, *,
         weights = torch.empty(shape, dtype=torch.float32, device=device)
     _dev_tensor(expert_ids, "expert_ids", torch.int32, shape, device)
     _dev_tensor(weights, "weights", torch.float32, shape, device)
-    st = load_library().moe_topk_packed_decode(_ptr(topk_packed), topk_packed.numel(),
-                                               _ptr(expert_ids), _ptr(weights),
-                                               _stream(device))
-    _check("moe_topk_packed_decode", st)
+    _call("moe_topk_packed_decode", device, _ptr(topk_packed), topk_packed.numel(),
+          _ptr(expert_ids), _ptr(weights))
     return expert_ids, weights
 
 
@@ -289,10 +291,8 @@ def moe_topk_sigmoid_gate(router_logits: torch.Tensor, top_k: int, *,
         _tensor(topk_packed, "topk_packed", torch.int32, shape)
     _on_device(device, router_logits=router_logits, topk_ids=topk_ids,
                topk_weights=topk_weights, topk_packed=topk_packed)
-    st = load_library().moe_topk_sigmoid_gate(_ptr(router_logits), T, E, int(top_k),
-                                              _ptr(topk_ids), _ptr(topk_weights),
-                                              _ptr(topk_packed), _stream(device))
-    _check("moe_topk_sigmoid_gate", st)
+    _call("moe_topk_sigmoid_gate", device, _ptr(router_logits), T, E, int(top_k),
+          _ptr(topk_ids), _ptr(topk_weights), _ptr(topk_packed))
     return topk_ids, topk_weights, topk_packed
 
 
@@ -313,9 +313,7 @@ def _act_quant(fn_name, x, out_e4m3, scale, scale_dtype):
     _tensor(out_e4m3, "out_e4m3", torch.uint8, (T, H))
     _tensor(scale, "scale", scale_dtype, (T, H // QUANT_BLOCK))
     _on_device(device, x=x, out_e4m3=out_e4m3, scale=scale)
-    st = getattr(load_library(), fn_name)(_ptr(x), T, H, _ptr(out_e4m3), _ptr(scale),
-                                          _stream(device))
-    _check(fn_name, st)
+    _call(fn_name, device, _ptr(x), T, H, _ptr(out_e4m3), _ptr(scale))
     return out_e4m3, scale
 
 
@@ -346,7 +344,6 @@ def moe_finalize_ep_combine(partials: torch.Tensor, *,
         out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
     _tensor(out, "out", torch.bfloat16, (T, H))
     _on_device(device, partials=partials, shared_out=shared_out, out=out)
-    st = load_library().moe_finalize_ep_combine(_ptr(partials), R, _ptr(shared_out), _ptr(out),
-                                                T, H, _stream(device))
-    _check("moe_finalize_ep_combine", st)
+    _call("moe_finalize_ep_combine", device, _ptr(partials), R, _ptr(shared_out), _ptr(out),
+          T, H)
     return out
