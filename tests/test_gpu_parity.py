@@ -58,15 +58,16 @@ def test_tiny_config(packed):
     check_finalize(wl, got, packed=packed, what="tiny")
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("T", [1, 4, 8, 16, 64, 256])
-def test_decode_sweep(T):
+def test_decode_sweep(T, packed):
     wl = W.config_workload(1, T)
-    announce(f"decode sweep T={T} H=4096 k=8")
+    announce(f"decode sweep T={T} H=4096 k=8 packed={packed}")
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    got = run_finalize(wl, err=err)
+    got = run_finalize(wl, packed=packed, err=err)
     assert int(err.item()) == 0
     assert np.isfinite(F.bf16_to_f64(got)).all()          # NaN padding never read
-    check_finalize(wl, got, what=f"decode T={T}")
+    check_finalize(wl, got, packed=packed, what=f"decode T={T}")
 
 
 def test_packed_vs_unpacked_full_size():
@@ -86,16 +87,17 @@ def test_packed_vs_unpacked_full_size():
     assert not np.array_equal(pk, up)        # genuine fp32 weights differ
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("T", [16, 256, 1024])
-def test_residual_rmsnorm(T):
+def test_residual_rmsnorm(T, packed):
     wl = W.config_workload(3, T)
-    announce(f"residual+rmsnorm T={T} H=7168 k=8")
-    kw = device_inputs(wl)
+    announce(f"residual+rmsnorm T={T} H=7168 k=8 packed={packed}")
+    kw = device_inputs(wl, packed=packed)
     ro, nm = M.moe_finalize_residual_rmsnorm(**kw, residual=d_bf16(wl.residual),
                                              gamma=d_bf16(wl.gamma), eps=wl.eps)
     torch.cuda.synchronize()
     ro, nm = h_bits(ro), h_bits(nm)
-    check_rmsnorm(wl, ro, nm)
+    check_rmsnorm(wl, ro, nm, packed=packed)
 
 
 def check_rmsnorm(wl, ro, nm, packed=False):
@@ -125,10 +127,16 @@ def check_rmsnorm(wl, ro, nm, packed=False):
     assert np.all(np.abs(g - o) <= 2e-2 * np.abs(o) + slack)
 
 
-def test_prefill_quant_full_size():
-    wl = W.config_workload(4)
-    announce("prefill quant T=8192 H=7168 k=8")
-    kw = device_inputs(wl)
+@pytest.fixture(scope="module")
+def prefill_workload():
+    return W.config_workload(4)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_prefill_quant_full_size(prefill_workload, packed):
+    wl = prefill_workload
+    announce(f"prefill quant T=8192 H=7168 k=8 packed={packed}")
+    kw = device_inputs(wl, packed=packed)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     q, s = M.moe_finalize_quant_ue8m0(**kw, err_flag=err)
     torch.cuda.synchronize()
@@ -136,7 +144,7 @@ def test_prefill_quant_full_size():
     q, s = h_u8(q), h_u8(s)
     del kw
     torch.cuda.empty_cache()
-    check_quant(wl, q, s)
+    check_quant(wl, q, s, packed=packed)
 
 
 def check_quant(wl, q, s, packed=False, with_shared=True, chunk=512):
