@@ -11,6 +11,17 @@
 //    an all-zero block), q = e4m3(x / s) (fp32 division, then the plain E4M3
 //    converter, nearest even), the scale stored as float32.
 //
+// The continuous policy needs one correctly rounded fp32 quotient per element.
+// The compiler's IEEE division is 11 VALU ops, which made this kernel
+// ALU-bound. Here it is 5 FMA-unit ops per element: one IEEE reciprocal
+// y = fl(1/s) per lane, then div_rn below (Markstein's refinement, P. W.
+// Markstein, "Computation of elementary functions on the IBM RISC System/6000
+// processor", IBM J. Res. Dev. 34(1), 1990). The result is bit-identical to
+// the IEEE quotient whenever the operands and residuals are normal fp32
+// numbers. Outside that, |x| < 2^-100 with s >= 2^-60, so both quotients are
+// below 2^-40 and encode to the same signed zero. Blocks whose scale falls
+// outside [2^-60, 2^60] keep the IEEE division.
+//
 // One wavefront per (token, 512 columns): each lane loads 8 bf16 (16 bytes),
 // a 1 x 128 block is one 16-lane DPP row. HBM-bound: 2 bytes read and 1 byte
 // written per element, plus the scales.
@@ -22,6 +33,21 @@ namespace moef {
 namespace {
 
 using namespace dev;
+
+// fl(x / s), the correctly rounded quotient, given y = fl(1 / s) and s in
+// [2^-60, 2^60]:
+//  * q1 = fl(x y) is within 1.5 ulp of x/s;
+//  * one residual step makes q2 faithful (within 1 ulp);
+//  * with y within half an ulp of 1/s and q2 faithful, the residual
+//    x - s q2 is exact and fl(q2 + (x - s q2) y) = fl(x/s) (Markstein).
+// copysign restores the sign of a zero quotient, which a cancelling final sum
+// would make +0.
+__device__ __forceinline__ float div_rn(float x, float s, float y) {
+  const float q1 = x * y;
+  const float q2 = __builtin_fmaf(__builtin_fmaf(-s, q1, x), y, q1);
+  const float q3 = __builtin_fmaf(__builtin_fmaf(-s, q2, x), y, q2);
+  return __builtin_copysignf(q3, x);
+}
 
 template <bool POW2>
 __global__ void __launch_bounds__(kWavesPerBlock * kWaveLanes)
@@ -50,8 +76,14 @@ act_quant_kernel(const u32x4* __restrict__ x, int tokens, int h8, int nchunks,
     const float s = a > 0.0f ? a / 448.0f : 1.0f;
     float f[8];
     unpack8(v, f);
+    if (s >= 0x1p-60f && s <= 0x1p60f) {        // block-uniform: whole 16-lane rows
+      const float y = 1.0f / s;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = f[e] / s;
+      for (int e = 0; e < 8; ++e) f[e] = div_rn(f[e], s, y);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = f[e] / s;
+    }
     int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
     int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);

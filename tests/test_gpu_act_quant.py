@@ -99,3 +99,57 @@ def test_policies_agree_on_power_of_two_blocks():
     assert np.array_equal(q1, q2)
     assert np.array_equal(s1.astype(np.int64) - 127, m)
     assert np.array_equal(s2, np.exp2(m).astype(np.float32))
+
+
+def blocks_under_maxima(maxima):
+    """Blocks of 128: the maximum A first, then every finite bf16 x with |x| <= A
+    (127 per block, the last block padded with zeros)."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = F.bf16_to_f64(pats)
+    out = []
+    for a in maxima:
+        A = F.bf16_to_f64(np.array([a], np.uint16))[0]
+        xs = pats[np.isfinite(v) & (np.abs(v) <= A)]
+        nblk = -(-xs.size // 127)
+        b = np.zeros((nblk, 128), np.uint16)
+        flat = np.zeros(nblk * 127, np.uint16)
+        flat[:xs.size] = xs
+        b[:, 1:] = flat.reshape(nblk, 127)
+        b[:, 0] = a
+        out.append(b)
+    return np.concatenate(out)
+
+
+def test_continuous_scale_every_value_under_sampled_maxima():
+    """The continuous policy's quotient x / s against the oracle's IEEE fp32
+    division, bit for bit through the codes, for every bf16 x under sampled
+    block maxima A:
+      * A whose mantissa has a factor 7 (1.75, 1.3125, 1.09375 times 2^k),
+        so s = A/448 is short and many quotients sit exactly on E4M3 midpoints;
+      * random A;
+      * A whose scale sits on either side of 2^-60 and 2^60, where the
+        kernel switches between its two division paths;
+      * the smallest and largest A (subnormal and huge scales)."""
+    rng = np.random.default_rng(21)
+    sevens = []
+    for m in (1.75, 1.3125, 1.09375):
+        for k in rng.integers(-120, 120, size=20):
+            sevens.append(m * 2.0 ** int(k))
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = F.bf16_to_f64(pats)
+    pos = pats[np.isfinite(v) & (v > 0)]
+    edges = []
+    for e in (-60, 60):
+        b = int(F.bf16_bits(np.array([448.0 * 2.0 ** e]))[0])
+        edges += [b - 2, b - 1, b, b + 1, b + 2]
+    maxima = np.concatenate([F.bf16_bits(np.array(sevens)), rng.choice(pos, 200, replace=False),
+                             np.array(edges, np.uint16),
+                             np.array([0x0001, 0x0080, 0x7F7F], np.uint16)])
+    blocks = blocks_under_maxima(maxima)
+    H = 7168
+    T = -(-blocks.shape[0] // (H // 128))
+    rows = np.zeros((T * (H // 128), 128), np.uint16)
+    rows[:blocks.shape[0]] = blocks
+    x = rows.reshape(T, H)
+    announce(f"act quant continuous scale, {maxima.size} maxima, T={T}")
+    check_both(x, run_both(x))
