@@ -11,13 +11,18 @@
 // weights are the chosen sigmoids divided by their sum, in fp32.
 //
 // One wavefront per token. A lane holds up to 8 of the token's E <= 512
-// logits in registers, each as a 64-bit key (order-preserving image of the
-// logit above the complemented expert id), so one unsigned compare implements
-// the whole order. Each of the top_k rounds takes every lane's best live key,
-// the maximum inside each 16-lane row by four DPP steps, and the four row
-// maxima read into scalar registers: the winner is uniform with no LDS or
-// memory traffic. Lane r keeps round r's winner. Lanes 0..top_k-1 then
-// evaluate their sigmoid, the wave sums them, and each writes its slot.
+// logits in registers as 32-bit order keys: an order-preserving image of the
+// logit, with NaN mapped to 1 (below -inf) and "no candidate" to 0. Each of
+// the top_k rounds takes
+//  * every lane's largest live key;
+//  * the maximum inside each 16-lane row, by four DPP rotate-and-max steps;
+//  * the maximum of the four row maxima, read into scalar registers.
+// Equal keys are then told apart without memory traffic: one ballot per
+// register slot j marks the lanes that hold the maximum, and the first slot
+// with a mark, then its lowest lane, is the lowest expert id (expert =
+// lane + 64 j), which is the tie rule. Lane r keeps round r's winner. Lanes
+// 0..top_k-1 then evaluate their sigmoid, the wave sums them, and each writes
+// its slot.
 
 #include "device_common.h"
 #include "moef_internal.h"
@@ -29,65 +34,19 @@ using namespace dev;
 
 constexpr int kGateWaves = 4;
 
-// Order-preserving 32-bit image of a logit: larger value -> larger image;
-// -0 and +0 map together; NaN maps to 0, below -inf.
-__device__ __forceinline__ uint32_t order_bits(float v) {
-  if (v != v) return 0u;
+// Order-preserving 32-bit image of a logit: a larger value gives a larger
+// key; -0 and +0 map together; NaN maps to 1, below -inf (0x007FFFFF);
+// 0 is left for "no candidate".
+__device__ __forceinline__ uint32_t gate_key(float v) {
+  if (v != v) return 1u;
   const uint32_t u = v == 0.0f ? 0u : __float_as_uint(v);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inverse of order_bits for non-NaN images (0 -> NaN).
-__device__ __forceinline__ float from_order_bits(uint32_t o) {
-  if (o == 0u) return __builtin_nanf("");
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-
-// Candidate key: a larger key comes first (larger logit, then lower id).
-// 0 means "no candidate".
-__device__ __forceinline__ uint64_t cand_key(float v, int e) {
-  return ((uint64_t)order_bits(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
-__device__ __forceinline__ uint64_t dpp_max(uint64_t k, int ctrl_sel) {
-  uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
-  uint32_t olo, ohi;
-  switch (ctrl_sel) {   // constant after unrolling
-    case 0:
-      olo = __builtin_amdgcn_mov_dpp((int)lo, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
-      ohi = __builtin_amdgcn_mov_dpp((int)hi, 0xB1, 0xF, 0xF, false);
-      break;
-    case 1:
-      olo = __builtin_amdgcn_mov_dpp((int)lo, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
-      ohi = __builtin_amdgcn_mov_dpp((int)hi, 0x4E, 0xF, 0xF, false);
-      break;
-    case 2:
-      olo = __builtin_amdgcn_mov_dpp((int)lo, 0x124, 0xF, 0xF, false);  // row_ror:4
-      ohi = __builtin_amdgcn_mov_dpp((int)hi, 0x124, 0xF, 0xF, false);
-      break;
-    default:
-      olo = __builtin_amdgcn_mov_dpp((int)lo, 0x128, 0xF, 0xF, false);  // row_ror:8
-      ohi = __builtin_amdgcn_mov_dpp((int)hi, 0x128, 0xF, 0xF, false);
-      break;
-  }
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > k ? o : k;
-}
-
-// The largest key of the wave, uniform: DPP maxima inside each 16-lane row,
-// then the four row maxima read into scalar registers.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) k = dpp_max(k, c);
-  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
-  uint64_t best = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint64_t rk = ((uint64_t)__builtin_amdgcn_readlane(hi, 16 * r) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane(lo, 16 * r);
-    best = rk > best ? rk : best;
-  }
-  return best;
+// The logit a key came from (+0 for a zero, NaN for key 1).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  if (k == 1u) return __builtin_nanf("");
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 template <int EPL>
@@ -101,27 +60,40 @@ topk_sigmoid_gate_kernel(const float* __restrict__ logits, int tokens, int exper
   if (t >= tokens) return;                       // whole waves
   const float* row = logits + (int64_t)t * experts;
 
-  uint64_t key[EPL];
+  uint32_t key[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + j * kWaveLanes;
-    key[j] = e < experts ? cand_key(row[e], e) : 0u;
+    key[j] = e < experts ? gate_key(row[e]) : 0u;
   }
 
-  uint64_t mine = 0;                             // lane r keeps round r's winner
+  uint32_t my_key = 0;                           // lane r keeps round r's winner
+  int my_id = 0;
   for (int r = 0; r < k; ++r) {
-    uint64_t b = key[0];
+    uint32_t b = key[0];
 #pragma unroll
-    for (int j = 1; j < EPL; ++j) b = key[j] > b ? key[j] : b;
-    const uint64_t win = wave_max_key(b);        // uniform
-    if (lane == r) mine = win;
+    for (int j = 1; j < EPL; ++j) b = max(b, key[j]);
+    b = row16_max(b);
+    const uint32_t m = max(max((uint32_t)__builtin_amdgcn_readlane((int)b, 0),
+                               (uint32_t)__builtin_amdgcn_readlane((int)b, 16)),
+                           max((uint32_t)__builtin_amdgcn_readlane((int)b, 32),
+                               (uint32_t)__builtin_amdgcn_readlane((int)b, 48)));
+    // k <= live candidates, so m >= 1 and some slot holds it
+    int wj = EPL - 1;
+    uint64_t hit = 0;
+#pragma unroll
+    for (int j = EPL - 1; j >= 0; --j) {         // ends on the first slot with a hit
+      const uint64_t bj = __ballot(key[j] == m);
+      if (bj != 0) { wj = j; hit = bj; }
+    }
+    const int wl = (int)__builtin_ctzll(hit);
+    if (lane == r) { my_key = m; my_id = wl + wj * kWaveLanes; }
 #pragma unroll
     for (int j = 0; j < EPL; ++j)
-      if (key[j] == win) key[j] = 0u;            // keys are unique: one lane, one slot
+      if (j == wj && lane == wl) key[j] = 0u;
   }
 
-  const int my_id = (int)(0xFFFFFFFFu - (uint32_t)mine);
-  const float my_v = from_order_bits((uint32_t)(mine >> 32));
+  const float my_v = key_value(my_key);
   const float s = lane < k ? 1.0f / (1.0f + expf(-my_v)) : 0.0f;
   float sum = s;
 #pragma unroll

@@ -59,16 +59,20 @@ def test_gate_random(T, E, k):
     check_gate(l, k, *run_gate(l, k))
 
 
-def test_gate_ties_specials_and_equal_logits():
-    rng = np.random.default_rng(31)
-    l = rng.integers(-3, 4, size=(400, 64)).astype(np.float32)   # many exact ties
+@pytest.mark.parametrize("E", [64, 100, 256, 512])
+def test_gate_ties_specials_and_equal_logits(E):
+    """Exact ties inside and across a lane's register slots (E > 64 puts
+    experts e and e + 64 in one lane), NaN, +-inf, -0, all-equal and all-NaN
+    rows."""
+    rng = np.random.default_rng(31 + E)
+    l = rng.integers(-3, 4, size=(400, E)).astype(np.float32)    # many exact ties
     l[::9, 7] = np.nan
     l[::5, 11] = -np.inf
     l[::6, 12] = np.inf
     l[::4, 13] = -0.0
     l[1] = 0.5                                                     # all equal
     l[2] = np.nan                                                  # all NaN
-    announce("gate ties and specials")
+    announce(f"gate ties and specials E={E}")
     ids, w, pk = run_gate(l, 8)
     oid, ow, _ = R.topk_sigmoid_gate(l, 8)
     assert np.array_equal(ids, oid)
