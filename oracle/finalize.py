@@ -275,3 +275,44 @@ def ep_combine_truth(partials, shared=None):
     if shared is not None:
         acc = acc + F.bf16_to_f64(shared)
     return F.bf16_bits(acc)
+
+
+# ------------------------------------------------------------------------
+# All-reduce + residual + RMSNorm after the deferred finalize, one GPU's share.
+#
+# "[Kimi K2.5] Fuse deferred MoE finalize into next-layer AR + residual +
+# RMSNorm", "Numerics & speed vs the separate-finalize fallback": the
+# preferred path under graph-captured decode is the deferred finalize followed
+# by a separate all-reduce + residual + RMSNorm kernel that also emits
+# residual_out and accumulates in fp32 (the fused kernel's extra error comes
+# from accumulating inside the bf16 all-reduce pipeline). Readings:
+#   AR1  the R inputs are the ranks' bf16 finalize outputs for the same tokens
+#        (under TP each holds a partial sum; under EP each holds its slots);
+#        they are added in fp32 from +0 in rank order, then the residual, and
+#        the sum is rounded once to bf16: that is residual_out;
+#   AR2  the shared-expert output is already inside the ranks' outputs (each
+#        rank's finalize adds its own share), so it is not a separate input;
+#   AR3  normed is the RMSNorm of the stored bf16 residual_out (reading R5).
+# ------------------------------------------------------------------------
+
+def allreduce_residual_rmsnorm_mirror(partials, residual, gamma, eps=1e-6):
+    """(residual_out bits, normed bits) for bf16 rank outputs [R, T, H]:
+    acc = +0; acc = acc + partial_r for r ascending; acc = acc + residual;
+    residual_out = bf16(acc), in fp32 steps (readings AR1, AR2); normed is the
+    fp64 RMSNorm of residual_out (AR3; its reduction order is free)."""
+    p = np.asarray(partials, dtype=np.uint16)
+    acc = np.zeros(p.shape[1:], dtype=np.float32)
+    for r in range(p.shape[0]):
+        acc = acc + F.bf16_to_f32(p[r])
+    acc = acc + F.bf16_to_f32(residual)
+    ro = F.bf16_bits(acc)
+    return ro, rmsnorm_f64(ro, gamma, eps)
+
+
+def allreduce_residual_rmsnorm_truth(partials, residual, gamma, eps=1e-6):
+    """Same outputs with the rank sum and the residual add in float64 (one
+    rounding to bf16)."""
+    p = np.asarray(partials, dtype=np.uint16)
+    acc = F.bf16_to_f64(p).sum(axis=0) + F.bf16_to_f64(residual)
+    ro = F.bf16_bits(acc)
+    return ro, rmsnorm_f64(ro, gamma, eps)
