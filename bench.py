@@ -277,6 +277,20 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
     measure("ep_combine_R4", T, H, 0, T * H * 2 * (R + 2),
             lambda: M.moe_finalize_ep_combine(parts, shared_out=shp, out=ep_out), iters_big)
     del parts, shp, ep_out
+    R, H = 8, 7168
+    for T in (1, 16, 256, 2048):
+        ranks = [torch.from_numpy(W.activations(T, H, seed=30 + r, log2_mag=None).view(np.int16))
+                 .view(torch.bfloat16).to("cuda:0") for r in range(R)]
+        ares = torch.from_numpy(W.activations(T, H, seed=40, log2_mag=None).view(np.int16)).view(
+            torch.bfloat16).to("cuda:0")
+        agam = torch.ones(H, dtype=torch.bfloat16, device="cuda:0")
+        aro = torch.empty_like(ares)
+        anm = torch.empty_like(ares)
+        measure("allreduce_residual_rmsnorm_R8", T, H, 0, T * 2 * H * (R + 3) + 2 * H,
+                lambda: M.moe_allreduce_residual_rmsnorm(ranks, residual=ares, gamma=agam,
+                                                         residual_out=aro, normed=anm),
+                iters_big if T >= 2048 else iters_small)
+        del ranks, ares, aro, anm
     n = 8192 * 8
     pk = torch.from_numpy(W.config_workload(0).packed.reshape(-1).repeat(n // 2)).to("cuda:0")
     ids = torch.empty_like(pk)

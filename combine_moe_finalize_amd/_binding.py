@@ -50,6 +50,8 @@ _SIGNATURES = {
     "moe_act_quant_fp8_ue8m0": [c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_void_p],
     "moe_finalize_ep_combine": [c_void_p, c_i32, c_void_p, c_void_p, c_i64, c_i64, c_void_p],
     "moe_act_quant_fp8_amax": [c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_void_p],
+    "moe_allreduce_residual_rmsnorm": [ctypes.POINTER(c_void_p), c_i32, c_void_p, c_void_p, c_f32,
+                                       c_void_p, c_void_p, c_i64, c_i64, c_void_p],
     "moe_finalize_status_string": [ctypes.c_int],
     "moe_finalize_abi_version": [],
 }
@@ -347,3 +349,42 @@ def moe_finalize_ep_combine(partials: torch.Tensor, *,
     _call("moe_finalize_ep_combine", device, _ptr(partials), R, _ptr(shared_out), _ptr(out),
           T, H)
     return out
+
+
+def moe_allreduce_residual_rmsnorm(rank_outputs, *, residual: torch.Tensor, gamma: torch.Tensor,
+                                   eps: float = 1e-6,
+                                   residual_out: Optional[torch.Tensor] = None,
+                                   normed: Optional[torch.Tensor] = None):
+    """(residual_out, normed), both bf16 [T, H]: the R ranks' finalize outputs
+    summed in fp32 in rank order, plus the residual, rounded once; then the
+    RMSNorm of that residual_out. rank_outputs is a sequence of bf16 [T, H]
+    tensors (separate buffers, as peers' buffers would be) or one [R, T, H]
+    tensor. residual_out may be residual (in-place update)."""
+    if isinstance(rank_outputs, torch.Tensor):
+        if rank_outputs.dim() != 3:
+            raise ValueError("rank_outputs must be [ranks, tokens, hidden] or a sequence of "
+                             "[tokens, hidden] tensors")
+        ranks = list(rank_outputs.unbind(0))
+    else:
+        ranks = list(rank_outputs)
+    if not ranks or not isinstance(ranks[0], torch.Tensor) or ranks[0].dim() != 2:
+        raise ValueError("rank_outputs must hold at least one [tokens, hidden] tensor")
+    T, H = ranks[0].shape
+    device = ranks[0].device
+    named = {}
+    for i, t in enumerate(ranks):
+        named[f"rank_outputs[{i}]"] = _tensor(t, f"rank_outputs[{i}]", torch.bfloat16, (T, H))
+    _tensor(residual, "residual", torch.bfloat16, (T, H))
+    _tensor(gamma, "gamma", torch.bfloat16, (H,))
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    if normed is None:
+        normed = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    _tensor(residual_out, "residual_out", torch.bfloat16, (T, H))
+    _tensor(normed, "normed", torch.bfloat16, (T, H))
+    _on_device(device, residual=residual, gamma=gamma, residual_out=residual_out, normed=normed,
+               **named)
+    ptrs = (c_void_p * len(ranks))(*[t.data_ptr() for t in ranks])
+    _call("moe_allreduce_residual_rmsnorm", device, ptrs, len(ranks), _ptr(residual), _ptr(gamma),
+          float(eps), _ptr(residual_out), _ptr(normed), T, H)
+    return residual_out, normed

@@ -19,7 +19,8 @@ except ImportError:            # run as a script
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from _paths import CSRC, INCLUDE, LIB_DIR, LIB_PATH
 
-SOURCES = ["moef_api.hip", "finalize_kernels.hip", "routing_kernels.hip", "act_quant_kernels.hip"]
+SOURCES = ["moef_api.hip", "finalize_kernels.hip", "routing_kernels.hip", "act_quant_kernels.hip",
+           "allreduce_kernels.hip"]
 ARCH = "gfx950"
 
 

@@ -250,6 +250,42 @@ int moe_finalize_ep_combine(const uint16_t* partials, int32_t num_partials,
                                             hidden, static_cast<hipStream_t>(stream)));
 }
 
+int moe_allreduce_residual_rmsnorm(const uint16_t* const* rank_outputs, int32_t num_ranks,
+                                   const uint16_t* residual, const uint16_t* gamma, float eps,
+                                   uint16_t* residual_out, uint16_t* normed, int64_t num_tokens,
+                                   int64_t hidden, void* stream) {
+  if (num_tokens < 0 || hidden < 1 || num_ranks < 1 || num_ranks > MOEF_MAX_AR_RANKS)
+    return MOEF_ERR_BAD_SHAPE;
+  if (hidden % moef::kVecElems != 0 || hidden > MOEF_MAX_HIDDEN_RMSNORM ||
+      num_tokens > moef::kMaxUnits)
+    return MOEF_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOEF_OK;
+  if (rank_outputs == nullptr || residual == nullptr || gamma == nullptr ||
+      residual_out == nullptr || normed == nullptr)
+    return MOEF_ERR_NULL_POINTER;
+  for (int r = 0; r < num_ranks; ++r)
+    if (rank_outputs[r] == nullptr) return MOEF_ERR_NULL_POINTER;
+  for (int r = 0; r < num_ranks; ++r)
+    if (!aligned(rank_outputs[r], 16)) return MOEF_ERR_MISALIGNED;
+  if (!aligned(residual, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) ||
+      !aligned(normed, 16))
+    return MOEF_ERR_MISALIGNED;
+  const int64_t tb = num_tokens * hidden * 2;
+  Span s[MOEF_MAX_AR_RANKS + 3];
+  int ns = 0;
+  for (int r = 0; r < num_ranks; ++r) s[ns++] = {rank_outputs[r], tb};
+  s[ns++] = {gamma, hidden * 2};
+  // residual_out may be residual itself, but no other overlap is allowed
+  if (overlaps_any(residual_out, tb, s, ns)) return MOEF_ERR_BAD_ALIAS;
+  if (residual_out != residual && overlap(residual_out, tb, residual, tb)) return MOEF_ERR_BAD_ALIAS;
+  s[ns++] = {residual, tb};
+  if (overlaps_any(normed, tb, s, ns) || overlap(normed, tb, residual_out, tb))
+    return MOEF_ERR_BAD_ALIAS;
+  return hip_status(moef::launch_allreduce_rmsnorm(rank_outputs, num_ranks, residual, gamma, eps,
+                                                   residual_out, normed, num_tokens, hidden,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 int moe_topk_packed_decode(const int32_t* packed, int64_t n, int32_t* expert_ids,
                            float* weights, void* stream) {
   if (n < 0) return MOEF_ERR_BAD_SHAPE;

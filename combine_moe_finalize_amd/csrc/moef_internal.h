@@ -40,6 +40,11 @@ hipError_t launch_ep_combine(const uint16_t* partials, int32_t num_partials,
                              const uint16_t* shared, uint16_t* out, int64_t tokens,
                              int64_t hidden, hipStream_t stream);
 
+hipError_t launch_allreduce_rmsnorm(const uint16_t* const* rank_outputs, int32_t num_ranks,
+                                    const uint16_t* residual, const uint16_t* gamma, float eps,
+                                    uint16_t* residual_out, uint16_t* normed, int64_t tokens,
+                                    int64_t hidden, hipStream_t stream);
+
 hipError_t launch_packed_decode(const int32_t* packed, int64_t n,
                                 int32_t* expert_ids, float* weights,
                                 hipStream_t stream);

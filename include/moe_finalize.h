@@ -80,6 +80,7 @@ extern "C" {
 #define MOEF_QUANT_BLOCK 128         /* the UE8M0 epilogue needs hidden % 128 == 0 */
 #define MOEF_MAX_GATE_EXPERTS 512    /* the gate keeps a token's logits in registers */
 #define MOEF_MAX_EP_PARTIALS 64      /* partials one combine call may sum */
+#define MOEF_MAX_AR_RANKS 16         /* rank outputs one all-reduce call may sum */
 
 #define MOEF_DEVERR_INDEX_OUT_OF_RANGE 1
 
@@ -190,6 +191,45 @@ int moe_finalize_quant_ue8m0(const uint16_t* gemm2_out, int64_t num_rows,
 int moe_finalize_ep_combine(const uint16_t* partials, int32_t num_partials,
                             const uint16_t* shared_out, uint16_t* out,
                             int64_t num_tokens, int64_t hidden, void* stream);
+
+/*
+ * moe_allreduce_residual_rmsnorm - the part one GPU runs of the all-reduce +
+ * residual + RMSNorm that follows the deferred finalize when the MoE layer is
+ * split over R ranks. ("[Kimi K2.5] Fuse deferred MoE finalize into
+ * next-layer AR + residual + RMSNorm", Numerics & speed vs the
+ * separate-finalize fallback: the preferred path is the deferred finalize
+ * followed by an all-reduce + residual + RMSNorm kernel that emits
+ * residual_out and accumulates in fp32.) Each input is one rank's
+ * moe_finalize output: its tensor-parallel partial sum, or its
+ * expert-parallel slots. The shared-expert output is inside those outputs
+ * (each rank adds its share, or one rank adds all of it). On a multi-GPU node
+ * the pointers are the peers' buffers mapped into this process; on one GPU
+ * they are local buffers.
+ *
+ *  rank_outputs  host array of num_ranks device pointers, each bf16
+ *                [num_tokens, hidden]. The array is read during the call only;
+ *                the pointers go to the kernel by value.
+ *  num_ranks     R in [1, MOEF_MAX_AR_RANKS].
+ *  residual      bf16 [num_tokens, hidden].
+ *  gamma         bf16 [hidden].
+ *  residual_out  bf16 [num_tokens, hidden] = bf16(+0 + o_0 + ... + o_{R-1}
+ *                + residual): fp32 adds in that order, one rounding. May be
+ *                residual itself (in-place update), but no other overlap.
+ *  normed        bf16 [num_tokens, hidden] = bf16(residual_out *
+ *                rsqrt(mean(residual_out^2) + eps) * gamma), fp32 math; must
+ *                not overlap any input or residual_out.
+ *  hidden        a multiple of 8, at most MOEF_MAX_HIDDEN_RMSNORM.
+ *  num_tokens == 0 is a no-op.
+ *  Errors: R outside [1, MOEF_MAX_AR_RANKS], num_tokens < 0 or hidden < 1
+ *  give BAD_SHAPE; hidden not a multiple of 8, hidden above the limit or
+ *  num_tokens above 2^31 - 1 give UNSUPPORTED; a NULL array, rank pointer or
+ *  buffer gives NULL_POINTER; a pointer that is not 16-byte aligned gives
+ *  MISALIGNED; the overlaps above give BAD_ALIAS.
+ */
+int moe_allreduce_residual_rmsnorm(const uint16_t* const* rank_outputs, int32_t num_ranks,
+                                   const uint16_t* residual, const uint16_t* gamma, float eps,
+                                   uint16_t* residual_out, uint16_t* normed,
+                                   int64_t num_tokens, int64_t hidden, void* stream);
 
 /*
  * moe_topk_packed_decode - split packed routing words.

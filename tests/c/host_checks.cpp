@@ -122,6 +122,53 @@ int main() {
   check("ep combine T huge", moe_finalize_ep_combine(at<uint16_t>(G2), 4, nullptr,
                                                      at<uint16_t>(OUT), INT64_MAX, 8, nullptr),
         MOEF_ERR_UNSUPPORTED, false);
+  // all-reduce + residual + RMSNorm: rank buffers 2^46 bytes apart hold the
+  // largest accepted size (2^31 - 1 tokens of 16384 columns)
+  {
+    const uint16_t* ranks[MOEF_MAX_AR_RANKS + 1];
+    for (int r = 0; r <= MOEF_MAX_AR_RANKS; ++r)
+      ranks[r] = at<uint16_t>(0x1000000000000ull + (uint64_t)r * 0x400000000000ull);
+    const uint64_t top = 0x1000000000000ull + 0x400000000000ull * (MOEF_MAX_AR_RANKS + 1);
+    uint16_t* res = at<uint16_t>(top);
+    uint16_t* ro = at<uint16_t>(top + 0x400000000000ull);
+    uint16_t* nm = at<uint16_t>(top + 0x800000000000ull);
+    const uint16_t* gam = at<uint16_t>(0x1000);
+    check("allreduce ok", moe_allreduce_residual_rmsnorm(ranks, 8, res, gam, 1e-6f, ro, nm, 256,
+                                                         7168, nullptr), MOEF_OK, true);
+    check("allreduce largest sizes", moe_allreduce_residual_rmsnorm(
+        ranks, MOEF_MAX_AR_RANKS, res, gam, 1e-6f, ro, nm, INT32_MAX, 16384, nullptr),
+        MOEF_OK, true);
+    check("allreduce in place", moe_allreduce_residual_rmsnorm(ranks, 3, res, gam, 1e-6f, res, nm,
+                                                               16, 7168, nullptr), MOEF_OK, true);
+    check("allreduce T beyond 2^31 - 1", moe_allreduce_residual_rmsnorm(
+        ranks, 2, res, gam, 1e-6f, ro, nm, (int64_t)INT32_MAX + 1, 8, nullptr),
+        MOEF_ERR_UNSUPPORTED, false);
+    check("allreduce no ranks", moe_allreduce_residual_rmsnorm(ranks, 0, res, gam, 1e-6f, ro, nm,
+                                                               16, 7168, nullptr),
+          MOEF_ERR_BAD_SHAPE, false);
+    check("allreduce too many ranks", moe_allreduce_residual_rmsnorm(
+        ranks, MOEF_MAX_AR_RANKS + 1, res, gam, 1e-6f, ro, nm, 16, 7168, nullptr),
+        MOEF_ERR_BAD_SHAPE, false);
+    check("allreduce T=0", moe_allreduce_residual_rmsnorm(nullptr, 4, nullptr, nullptr, 1e-6f,
+                                                          nullptr, nullptr, 0, 7168, nullptr),
+          MOEF_OK, false);
+    const uint16_t* with_null[3] = {ranks[0], nullptr, ranks[2]};
+    check("allreduce NULL rank", moe_allreduce_residual_rmsnorm(with_null, 3, res, gam, 1e-6f, ro,
+                                                                nm, 16, 7168, nullptr),
+          MOEF_ERR_NULL_POINTER, false);
+    const uint16_t* odd[2] = {ranks[0], at<uint16_t>(0x1000000000000ull + 0x400000000000ull + 8)};
+    check("allreduce misaligned rank", moe_allreduce_residual_rmsnorm(odd, 2, res, gam, 1e-6f, ro,
+                                                                      nm, 16, 7168, nullptr),
+          MOEF_ERR_MISALIGNED, false);
+    check("allreduce normed overlaps a rank", moe_allreduce_residual_rmsnorm(
+        ranks, 4, res, gam, 1e-6f, ro, at<uint16_t>(0x1000000000000ull + 3 * 0x400000000000ull + 64),
+        16, 7168, nullptr), MOEF_ERR_BAD_ALIAS, false);
+    check("allreduce residual_out overlaps residual", moe_allreduce_residual_rmsnorm(
+        ranks, 4, res, gam, 1e-6f, res + 8, nm, 16, 7168, nullptr), MOEF_ERR_BAD_ALIAS, false);
+    check("allreduce H too large", moe_allreduce_residual_rmsnorm(ranks, 4, res, gam, 1e-6f, ro, nm,
+                                                                  16, 16392, nullptr),
+          MOEF_ERR_UNSUPPORTED, false);
+  }
   if (failures) {
     std::fprintf(stderr, "%d host check(s) failed\n", failures);
     return 1;

@@ -26,6 +26,12 @@ hipError_t launch_ep_combine(const uint16_t*, int32_t, const uint16_t*, uint16_t
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_allreduce_rmsnorm(const uint16_t* const*, int32_t, const uint16_t*,
+                                    const uint16_t*, float, uint16_t*, uint16_t*, int64_t, int64_t,
+                                    hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_act_quant(const uint16_t*, int64_t, int64_t, uint8_t*, uint8_t*, float*,
                             hipStream_t) {
   ++g_launches;

@@ -40,7 +40,8 @@ def test_exports_every_declared_symbol(lib):
                           "moe_finalize_quant_ue8m0", "moe_topk_packed_decode",
                           "moe_finalize_status_string", "moe_finalize_abi_version",
                           "moe_topk_sigmoid_gate", "moe_act_quant_fp8_ue8m0",
-                          "moe_act_quant_fp8_amax", "moe_finalize_ep_combine"}
+                          "moe_act_quant_fp8_amax", "moe_finalize_ep_combine",
+                          "moe_allreduce_residual_rmsnorm"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -210,3 +211,33 @@ def test_ep_combine_rules(lib):
     assert c(PP + 8, 4, SH, OUT, 4, 4096, None) == MISAL
     assert c(PP, 4, SH, PP + 3 * 4 * 4096 * 2, 4, 4096, None) == ALIAS   # out = last partial
     assert c(PP, 4, SH, SH, 4, 4096, None) == ALIAS
+
+
+def test_allreduce_rules(lib):
+    c = lib.moe_allreduce_residual_rmsnorm
+    T, H = 4, 4096
+    tb = T * H * 2
+
+    def ranks(*addrs):
+        return (ctypes.c_void_p * len(addrs))(*addrs)
+
+    rk = ranks(G2, G2 + 0x1_0000_0000, G2 + 0x2_0000_0000)
+    assert c(rk, 0, RES, GAM, 1e-6, RO, NRM, T, H, None) == SHAPE
+    assert c(rk, 17, RES, GAM, 1e-6, RO, NRM, T, H, None) == SHAPE
+    assert c(rk, 3, RES, GAM, 1e-6, RO, NRM, -1, H, None) == SHAPE
+    assert c(rk, 3, RES, GAM, 1e-6, RO, NRM, T, 0, None) == SHAPE
+    assert c(rk, 3, RES, GAM, 1e-6, RO, NRM, T, 4100, None) == UNSUP
+    assert c(rk, 3, RES, GAM, 1e-6, RO, NRM, T, 16392, None) == UNSUP
+    assert c(rk, 3, RES, GAM, 1e-6, RO, NRM, 2 ** 31, 8, None) == UNSUP
+    assert c(None, 3, RES, GAM, 1e-6, RO, NRM, 0, H, None) == OK          # empty batch
+    assert c(None, 3, RES, GAM, 1e-6, RO, NRM, T, H, None) == NULLP
+    assert c(ranks(G2, 0, G2 + 0x2_0000_0000), 3, RES, GAM, 1e-6, RO, NRM, T, H, None) == NULLP
+    assert c(rk, 3, None, GAM, 1e-6, RO, NRM, T, H, None) == NULLP
+    assert c(rk, 3, RES, GAM, 1e-6, RO, None, T, H, None) == NULLP
+    assert c(ranks(G2, G2 + 8), 2, RES, GAM, 1e-6, RO, NRM, T, H, None) == MISAL
+    assert c(rk, 3, RES, GAM + 4, 1e-6, RO, NRM, T, H, None) == MISAL
+    assert c(rk, 3, RES, GAM, 1e-6, G2 + 0x1_0000_0000 + 64, NRM, T, H, None) == ALIAS
+    assert c(rk, 3, RES, GAM, 1e-6, RES + 16, NRM, T, H, None) == ALIAS   # partial overlap
+    assert c(rk, 3, RES, GAM, 1e-6, RO, RO + tb - 16, T, H, None) == ALIAS
+    assert c(rk, 3, RES, GAM, 1e-6, RO, GAM, T, H, None) == ALIAS
+    assert c(rk, 3, RES, GAM, 1e-6, RO, G2 + 0x2_0000_0000, T, H, None) == ALIAS

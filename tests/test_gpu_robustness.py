@@ -104,6 +104,14 @@ def entry_points():
     b16, eo = guarded((5, 1000), torch.bfloat16)
     cases.append(("ep_combine", lambda: M.moe_finalize_ep_combine(parts, shared_out=shp, out=eo),
                   [eo], [b16]))
+
+    ranks = [d_bf16(W.activations(6, 7168, seed=20 + r, log2_mag=None)) for r in range(3)]
+    ares = d_bf16(W.activations(6, 7168, seed=24, log2_mag=None))
+    agam = d_bf16(W.activations(1, 7168, seed=25, log2_mag=None)[0])
+    b17, aro = guarded((6, 7168), torch.bfloat16)
+    b18, anm = guarded((6, 7168), torch.bfloat16)
+    cases.append(("allreduce", lambda: M.moe_allreduce_residual_rmsnorm(
+        ranks, residual=ares, gamma=agam, residual_out=aro, normed=anm), [aro, anm], [b17, b18]))
     return cases
 
 
