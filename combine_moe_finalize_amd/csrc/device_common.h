@@ -53,13 +53,31 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // ------------------------------------------- 1 x 128 block quantization
 
+// max(v, the value DPP control `ctrl` moves into this lane). Lanes whose row
+// `row_mask` leaves out get 0, the identity of an unsigned max, so they keep
+// v; the compiler folds the move into one v_max_u32 with a DPP source.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false));
+}
+
 // Largest value across the 16 lanes of a DPP row (every lane gets it).
 __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));   // row_ror:8
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));   // row_ror:4
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x122, 0xF, 0xF, false));   // row_ror:2
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x121, 0xF, 0xF, false));   // row_ror:1
+  v = dpp_umax<0x128, 0xF>(v);   // row_ror:8
+  v = dpp_umax<0x124, 0xF>(v);   // row_ror:4
+  v = dpp_umax<0x122, 0xF>(v);   // row_ror:2
+  v = dpp_umax<0x121, 0xF>(v);   // row_ror:1
   return v;
+}
+
+// Largest value across the wave, uniform. After the row maxima, row_bcast:15
+// folds each row's lane 15 into the next row (rows 1 and 3) and row_bcast:31
+// folds lane 31 into rows 2 and 3, so lane 63 holds the maximum of all four.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row16_max(v);
+  v = dpp_umax<0x142, 0xA>(v);   // row_bcast:15
+  v = dpp_umax<0x143, 0xC>(v);   // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Largest |y| of the eight bf16 values in v, as bf16 bits: with the sign

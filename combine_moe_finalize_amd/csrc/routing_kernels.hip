@@ -16,7 +16,8 @@
 // the top_k rounds takes
 //  * every lane's largest live key;
 //  * the maximum inside each 16-lane row, by four DPP rotate-and-max steps;
-//  * the maximum of the four row maxima, read into scalar registers.
+//  * the maximum of the four rows by two DPP row-broadcast steps, read from
+//    the last lane into a scalar register.
 // Equal keys are then told apart without memory traffic: one ballot per
 // register slot j marks the lanes that hold the maximum, and the first slot
 // with a mark, then its lowest lane, is the lowest expert id (expert =
@@ -73,11 +74,7 @@ topk_sigmoid_gate_kernel(const float* __restrict__ logits, int tokens, int exper
     uint32_t b = key[0];
 #pragma unroll
     for (int j = 1; j < EPL; ++j) b = max(b, key[j]);
-    b = row16_max(b);
-    const uint32_t m = max(max((uint32_t)__builtin_amdgcn_readlane((int)b, 0),
-                               (uint32_t)__builtin_amdgcn_readlane((int)b, 16)),
-                           max((uint32_t)__builtin_amdgcn_readlane((int)b, 32),
-                               (uint32_t)__builtin_amdgcn_readlane((int)b, 48)));
+    const uint32_t m = wave_max_u32(b);
     // k <= live candidates, so m >= 1 and some slot holds it
     int wj = EPL - 1;
     uint64_t hit = 0;
