@@ -1,0 +1,93 @@
+"""Host-side parts of bench.py (no GPU): the one-GPU rule, the loud failure
+without a GPU, the algorithmic byte models against a count taken from the
+workload's own arrays, and the rule that HBM traffic is reported only for the
+kernel source the counters were taken on."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+from combine_moe_finalize_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run_bench(*args):
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="")
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT,
+                          capture_output=True, text=True, timeout=300, env=env)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = run_bench("--gpus", "2", "--steps", "1", "--warmup", "0")
+    assert r.returncode == 2
+    assert "--gpus 2" in r.stderr and "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_no_gpu_fails_loudly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    r = run_bench("--steps", "1", "--warmup", "0", "--no-sweep", "--no-cpu-baseline")
+    assert r.returncode == 1
+    assert "needs a GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def counted_bytes(wl, with_shared, outputs):
+    """Bytes the method must move, counted from the arrays themselves: the
+    gathered rows (one per live slot), the shared rows, the index and weight
+    rows, and the outputs."""
+    live = int(np.count_nonzero(wl.idx >= 0))
+    row = wl.gemm2_out.shape[1] * wl.gemm2_out.itemsize
+    n = live * row + wl.idx.nbytes + wl.weights.nbytes
+    if with_shared:
+        n += wl.shared.nbytes
+    return n + outputs
+
+
+@pytest.mark.parametrize("with_shared", [True, False])
+def test_byte_models_match_a_direct_count(with_shared):
+    wl = W.make_workload(64, 1024, 16, 8, rsf=1.0, seed=1, with_residual=True)
+    T, H, k = wl.T, wl.H, wl.top_k
+    plain = counted_bytes(wl, with_shared, T * H * 2)
+    assert bench.bytes_plain(T, H, k, shared=with_shared) == plain
+    rms = counted_bytes(wl, with_shared, 2 * T * H * 2) + wl.residual.nbytes + wl.gamma.nbytes
+    assert bench.bytes_rmsnorm(T, H, k, shared=with_shared) == rms
+    quant = counted_bytes(wl, with_shared, T * H + T * (H // 128))
+    assert bench.bytes_quant(T, H, k, shared=with_shared) == quant
+
+
+def test_headline_bytes_per_launch():
+    """The prefill figure quoted with the roofline: 136 312 B per token."""
+    assert bench.bytes_quant(8192, 7168, 8) == 1_116_667_904
+    assert bench.bytes_quant(1, 7168, 8) == 136_312
+
+
+def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
+    good = {"kernel_source_sha256": bench.kernel_source_hash(), "hbm_bytes_per_launch": 123}
+    p = tmp_path / "c.json"
+    p.write_text(json.dumps(good))
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(p))
+    assert bench.counters_traffic() == 123
+    p.write_text(json.dumps(dict(good, kernel_source_sha256="0" * 64)))
+    assert bench.counters_traffic() is None
+    p.write_text("not json")
+    assert bench.counters_traffic() is None
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(tmp_path / "missing.json"))
+    assert bench.counters_traffic() is None
+
+
+def test_committed_counters_match_the_committed_source():
+    """The counter summary in the repository was taken on the kernel sources
+    in the repository, so the bench line carries traffic."""
+    with open(bench.COUNTERS_FILE) as f:
+        c = json.load(f)
+    assert c["kernel_source_sha256"] == bench.kernel_source_hash()
+    assert c["algorithmic_bytes_per_launch"] == bench.bytes_quant(8192, 7168, 8)
+    assert 1.0 <= c["traffic_over_algorithmic"] < 1.05
