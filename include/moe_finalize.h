@@ -8,6 +8,10 @@
  * shared-expert output and writes bf16. Optional fused epilogues add the
  * residual and apply RMSNorm (emitting residual_out too), or quantize the
  * result to FP8 E4M3 with one power-of-two (UE8M0) scale per 1 x 128 block.
+ * Around it: the sigmoid top-k gate that produces the routing, a standalone
+ * FP8 activation quant, the expert-parallel combine, and the all-reduce +
+ * residual + RMSNorm that follows the finalize when the layer is split over
+ * ranks (the part one GPU runs).
  *
  * Sources (sglang pull-request pages):
  *  - "Support deferred MoE finalize for MXFP4 and FP8 block-scale":
@@ -20,7 +24,8 @@
  *    [token, top_k]; a flat index caused out-of-bounds reads; workspaces are
  *    sized before graph capture and never grow inside it) and "Numerics &
  *    speed" (gathering from the padded permuted buffer; residual + RMSNorm
- *    with residual_out; fp32 accumulation).
+ *    with residual_out; fp32 accumulation; the separate finalize followed by
+ *    an all-reduce + residual + RMSNorm kernel as the preferred path).
  *  - "[FP8][MoE] Honor UE8M0 activation scales in Triton MoE": Motivation and
  *    "More context" (power-of-two FP32 activation scales, FP8 range 448).
  *  - "[Deepseek V4] Keep fp32 routing weights in the mxfp4 trtllm MoE":
