@@ -22,9 +22,16 @@
 // below 2^-40 and encode to the same signed zero. Blocks whose scale falls
 // outside [2^-60, 2^60] keep the IEEE division.
 //
-// One wavefront per (token, 512 columns): each lane loads 8 bf16 (16 bytes),
-// a 1 x 128 block is one 16-lane DPP row. HBM-bound: 2 bytes read and 1 byte
-// written per element, plus the scales.
+// The input is read as a flat run of 16-byte vectors (8 bf16 each). Since
+// hidden is a multiple of 128, every aligned group of 16 vectors is one
+// 1 x 128 block of one token, so a 16-lane DPP row is one block wherever a
+// wave starts. A wave takes 64 U consecutive vectors, U = 1 or 2, and issues
+// all U loads of a lane before any arithmetic: a lane with a single 16-byte
+// load in flight leaves too few bytes in flight to cover HBM latency once
+// every wave slot is busy. HBM-bound: 2 bytes read and 1 byte written per
+// element, plus the scales.
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "moef_internal.h"
@@ -49,28 +56,19 @@ __device__ __forceinline__ float div_rn(float x, float s, float y) {
   return __builtin_copysignf(q3, x);
 }
 
+// Quantizes one lane's 8 values (vector vi of the flat [T, H/8] view); the
+// lane's 16-lane DPP row is one 1 x 128 block. Whole rows share `active`.
 template <bool POW2>
-__global__ void __launch_bounds__(kWavesPerBlock * kWaveLanes)
-act_quant_kernel(const u32x4* __restrict__ x, int tokens, int h8, int nchunks,
-                 u32x2* __restrict__ out_q, uint8_t* __restrict__ scale_e8m0,
-                 float* __restrict__ scale_f32) {
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int lane = threadIdx.x & 63;
-  const int unit = (int)blockIdx.x * kWavesPerBlock + wave;
-  if ((int64_t)unit >= (int64_t)tokens * nchunks) return;      // whole waves
-  const int t = unit / nchunks;
-  const int colv = (unit - t * nchunks) * kWaveLanes + lane;
-  const bool active = colv < h8;                                // h8 % 16 == 0
-  const int64_t col = active ? colv : h8 - 1;
-
-  const u32x4 v = __builtin_nontemporal_load(x + (int64_t)t * h8 + col);
+__device__ __forceinline__ void quant_vector(const u32x4 v, bool active, int64_t vi, int lane,
+                                             u32x2* __restrict__ out_q,
+                                             uint8_t* __restrict__ scale_e8m0,
+                                             float* __restrict__ scale_f32) {
   const uint32_t amax = row16_max(active ? absmax8_bits(v) : 0u);
   u32x2 q;
   if (POW2) {
     const int ex = ue8m0_exponent(amax);
     q = e4m3x8_scaled(v, ue8m0_scale(ex));
-    if (active && (lane & 15) == 0)
-      scale_e8m0[(int64_t)t * (h8 >> 4) + (colv >> 4)] = (uint8_t)(ex + 127);
+    if (active && (lane & 15) == 0) scale_e8m0[vi >> 4] = (uint8_t)(ex + 127);
   } else {
     const float a = __uint_as_float(amax << 16);
     const float s = a > 0.0f ? a / 448.0f : 1.0f;
@@ -89,29 +87,57 @@ act_quant_kernel(const u32x4* __restrict__ x, int tokens, int h8, int nchunks,
     int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
     hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
     q = u32x2{(uint32_t)lo, (uint32_t)hi};
-    if (active && (lane & 15) == 0) scale_f32[(int64_t)t * (h8 >> 4) + (colv >> 4)] = s;
+    if (active && (lane & 15) == 0) scale_f32[vi >> 4] = s;
   }
-  if (active) __builtin_nontemporal_store(q, out_q + (int64_t)t * h8 + colv);
+  if (active) __builtin_nontemporal_store(q, out_q + vi);
+}
+
+template <bool POW2, int U>
+__global__ void __launch_bounds__(kWavesPerBlock * kWaveLanes)
+act_quant_kernel(const u32x4* __restrict__ x, int64_t n, u32x2* __restrict__ out_q,
+                 uint8_t* __restrict__ scale_e8m0, float* __restrict__ scale_f32) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int64_t base = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * (kWaveLanes * U);
+  if (base >= n) return;                                        // whole waves
+  u32x4 v[U];
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const int64_t vi = base + i * kWaveLanes + lane;
+    v[i] = __builtin_nontemporal_load(x + (vi < n ? vi : n - 1));
+  }
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const int64_t vi = base + i * kWaveLanes + lane;
+    quant_vector<POW2>(v[i], vi < n, vi, lane, out_q, scale_e8m0, scale_f32);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t tokens, int64_t hidden, uint8_t* out_q,
                             uint8_t* scale_e8m0, float* scale_f32, hipStream_t stream) {
-  const int h8 = (int)(hidden / kVecElems);
-  const int nchunks = (h8 + kWaveLanes - 1) / kWaveLanes;
-  const int64_t units = tokens * nchunks;
-  const dim3 grid((unsigned int)((units + kWavesPerBlock - 1) / kWavesPerBlock));
-  const dim3 block(kWavesPerBlock * kWaveLanes);
+  const int64_t n = tokens * (hidden / kVecElems);            // a multiple of 16
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   u32x2* q = reinterpret_cast<u32x2*>(out_q);
-  if (scale_e8m0 != nullptr)
-    hipLaunchKernelGGL(act_quant_kernel<true>, grid, block, 0, stream, xv, (int)tokens, h8,
-                       nchunks, q, scale_e8m0, scale_f32);
-  else
-    hipLaunchKernelGGL(act_quant_kernel<false>, grid, block, 0, stream, xv, (int)tokens, h8,
-                       nchunks, q, scale_e8m0, scale_f32);
-  return hipGetLastError();
+  const dim3 block(kWavesPerBlock * kWaveLanes);
+  auto go = [&](auto u) {
+    constexpr int U = decltype(u)::value;
+    const int64_t per_block = (int64_t)kWavesPerBlock * kWaveLanes * U;
+    const dim3 grid((unsigned int)((n + per_block - 1) / per_block));
+    if (scale_e8m0 != nullptr)
+      hipLaunchKernelGGL((act_quant_kernel<true, U>), grid, block, 0, stream, xv, n, q,
+                         scale_e8m0, scale_f32);
+    else
+      hipLaunchKernelGGL((act_quant_kernel<false, U>), grid, block, 0, stream, xv, n, q,
+                         scale_e8m0, scale_f32);
+    return hipGetLastError();
+  };
+  // Two vectors per lane once the input reaches 32 MiB (2^21 vectors): enough
+  // waves remain to fill the chip, and each has twice the bytes in flight.
+  // Below that, one vector per lane keeps more waves.
+  if (n >= kActQuantPairFrom) return go(std::integral_constant<int, 2>{});
+  return go(std::integral_constant<int, 1>{});
 }
 
 }  // namespace moef

@@ -63,6 +63,7 @@ constexpr int kVecElems = 8;                           // bf16 per 16-byte vecto
 constexpr int kChunkCols = kWaveLanes * kVecElems;     // columns per wave pass
 constexpr int kWavesPerBlock = 4;                      // plain / quant kernels
 constexpr int kNormMaxThreads = 1024;                  // RMSNorm: one block per token
+constexpr int64_t kActQuantPairFrom = int64_t(1) << 21;  // act quant: 2 vectors per lane
 constexpr int64_t kMaxUnits = (int64_t(1) << 31) - 1;  // (token, chunk) pairs
 
 }  // namespace moef
