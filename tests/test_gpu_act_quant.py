@@ -56,6 +56,17 @@ def test_shapes(T, H):
     check_both(x, run_both(x))
 
 
+@pytest.mark.parametrize("T,H", [(131077, 128), (2340, 7168), (2341, 7168)])
+def test_two_vectors_per_lane_threshold_and_tail(T, H):
+    """Inputs of at least 2^21 16-byte vectors take two vectors per lane.
+    T=131077, H=128 is just above that with a last wave half-filled in its
+    first vector (64 lanes) and partly in its second (16 lanes); T=2340 and
+    2341 at H=7168 sit on either side of the threshold."""
+    x = W.activations(T, H, seed=T + H)
+    announce(f"act quant threshold/tail T={T} H={H} vectors={T * H // 8}")
+    check_both(x, run_both(x), chunk=max(1, (1 << 20) // H))
+
+
 def test_exhaustive_values_and_scales():
     """Every finite bf16 value in [-448, 448] inside blocks whose max is 448;
     then every positive finite bf16 as a block max with random others, and an
