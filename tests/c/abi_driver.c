@@ -3,16 +3,18 @@
  *
  * Reads a finalize workload from a directory written by the test suite,
  * runs moe_finalize (fp32 and packed weights) and moe_finalize_quant_ue8m0
- * through the C ABI on a HIP stream it creates, and writes the outputs back
- * for the test to compare with the CPU oracle. It also checks that rejected
- * calls return their documented status before touching the GPU.
+ * through the C ABI on a HIP stream it creates, then hands the two finalize
+ * outputs, as two ranks' outputs, to moe_allreduce_residual_rmsnorm (a host
+ * array of device pointers, the shared output as the residual). It writes the
+ * outputs back for the test to compare with the CPU oracle, and checks that
+ * rejected calls return their documented status before touching the GPU.
  *
  * usage: abi_driver DIR
  *   DIR/meta.txt : "T H K P rsf"
  *   DIR/g2.bin (uint16 P*H) idx.bin (int32 T*K) w.bin (float T*K)
- *   DIR/packed.bin (int32 T*K) shared.bin (uint16 T*H)
+ *   DIR/packed.bin (int32 T*K) shared.bin (uint16 T*H) gamma.bin (uint16 H)
  *   -> DIR/out.bin, out_packed.bin (uint16 T*H), q.bin (uint8 T*H),
- *      s.bin (uint8 T*H/128), err.bin (int32)
+ *      s.bin (uint8 T*H/128), err.bin (int32), ro.bin, nm.bin (uint16 T*H)
  */
 #include <stdint.h>
 #include <stdio.h>
@@ -104,9 +106,11 @@ int main(int argc, char** argv) {
   void* h_w = read_file(dir, "w.bin", slots * 4);
   void* h_pk = read_file(dir, "packed.bin", slots * 4);
   void* h_sh = read_file(dir, "shared.bin", (size_t)T * row);
-  if (!h_g2 || !h_idx || !h_w || !h_pk || !h_sh) return 6;
+  void* h_gam = read_file(dir, "gamma.bin", row);
+  if (!h_g2 || !h_idx || !h_w || !h_pk || !h_sh || !h_gam) return 6;
 
-  void *d_g2, *d_idx, *d_w, *d_pk, *d_sh, *d_out, *d_outp, *d_q, *d_s, *d_err;
+  void *d_g2, *d_idx, *d_w, *d_pk, *d_sh, *d_out, *d_outp, *d_q, *d_s, *d_err, *d_gam, *d_ro,
+      *d_nm;
   CHECK_HIP(hipMalloc(&d_g2, (size_t)P * row));
   CHECK_HIP(hipMalloc(&d_idx, slots * 4));
   CHECK_HIP(hipMalloc(&d_w, slots * 4));
@@ -117,6 +121,10 @@ int main(int argc, char** argv) {
   CHECK_HIP(hipMalloc(&d_q, (size_t)(T * H)));
   CHECK_HIP(hipMalloc(&d_s, (size_t)(T * (H / 128)) + 1));
   CHECK_HIP(hipMalloc(&d_err, 4));
+  CHECK_HIP(hipMalloc(&d_gam, row));
+  CHECK_HIP(hipMalloc(&d_ro, (size_t)T * row));
+  CHECK_HIP(hipMalloc(&d_nm, (size_t)T * row));
+  CHECK_HIP(hipMemcpy(d_gam, h_gam, row, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(d_g2, h_g2, (size_t)P * row, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(d_idx, h_idx, slots * 4, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(d_w, h_w, slots * 4, hipMemcpyHostToDevice));
@@ -134,6 +142,18 @@ int main(int argc, char** argv) {
     bad |= expect(moe_finalize_quant_ue8m0(d_g2, P, d_idx, d_w, NULL, d_sh, rsf, d_q, d_s, T, H,
                                            (int32_t)K, d_err, stream),
                   MOEF_OK, "moe_finalize_quant_ue8m0");
+  {
+    const uint16_t* ranks[2] = {(const uint16_t*)d_out, (const uint16_t*)d_outp};
+    bad |= expect(moe_allreduce_residual_rmsnorm(NULL, 2, d_sh, d_gam, 1e-6f, d_ro, d_nm, T, H,
+                                                 stream),
+                  MOEF_ERR_NULL_POINTER, "all-reduce without a rank array");
+    bad |= expect(moe_allreduce_residual_rmsnorm(ranks, 0, d_sh, d_gam, 1e-6f, d_ro, d_nm, T, H,
+                                                 stream),
+                  MOEF_ERR_BAD_SHAPE, "all-reduce with no ranks");
+    bad |= expect(moe_allreduce_residual_rmsnorm(ranks, 2, d_sh, d_gam, 1e-6f, d_ro, d_nm, T, H,
+                                                 stream),
+                  MOEF_OK, "moe_allreduce_residual_rmsnorm");
+  }
   CHECK_HIP(hipStreamSynchronize(stream));
   if (bad) return 7;
 
@@ -151,11 +171,16 @@ int main(int argc, char** argv) {
   }
   CHECK_HIP(hipMemcpy(&err, d_err, 4, hipMemcpyDeviceToHost));
   if (write_file(dir, "err.bin", &err, 4)) return 8;
+  CHECK_HIP(hipMemcpy(h_out, d_ro, (size_t)T * row, hipMemcpyDeviceToHost));
+  if (write_file(dir, "ro.bin", h_out, (size_t)T * row)) return 8;
+  CHECK_HIP(hipMemcpy(h_out, d_nm, (size_t)T * row, hipMemcpyDeviceToHost));
+  if (write_file(dir, "nm.bin", h_out, (size_t)T * row)) return 8;
 
   CHECK_HIP(hipStreamDestroy(stream));
   hipFree(d_g2); hipFree(d_idx); hipFree(d_w); hipFree(d_pk); hipFree(d_sh);
   hipFree(d_out); hipFree(d_outp); hipFree(d_q); hipFree(d_s); hipFree(d_err);
-  free(h_g2); free(h_idx); free(h_w); free(h_pk); free(h_sh); free(h_out);
+  hipFree(d_gam); hipFree(d_ro); hipFree(d_nm);
+  free(h_g2); free(h_idx); free(h_w); free(h_pk); free(h_sh); free(h_gam); free(h_out);
   printf("abi_driver: ok\n");
   return 0;
 }
