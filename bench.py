@@ -233,6 +233,12 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
         measure("decode", T, wl.H, wl.top_k, bytes_plain(T, wl.H, wl.top_k),
                 lambda: M.moe_finalize(**kw, out=out), iters_small)
+    for T in (1, 16):                      # the Kimi K2.5 decode shape (H 7168, 384 experts)
+        wl = W.make_workload(T, 7168, 384, 8, rsf=2.5, seed=W.default_seed(9, T))
+        kw, _ = upload(wl, torch)
+        out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
+        measure("decode_H7168_E384", T, wl.H, wl.top_k, bytes_plain(T, wl.H, wl.top_k),
+                lambda: M.moe_finalize(**kw, out=out), iters_small)
     wl = W.config_workload(2)
     for packed in (False, True):
         kw, _ = upload(wl, torch, packed=packed)
