@@ -78,6 +78,9 @@ int make_routed(Routed* r, const uint16_t* gemm2_out, int64_t num_rows, const in
   return MOEF_OK;
 }
 
+// Index of err_flag's own range in the list routed_spans() builds.
+constexpr int kErrSpan = 4;
+
 // The input byte ranges of a routed call (for alias checks).
 int routed_spans(const Routed& r, Span* s) {
   const int64_t row_bytes = r.hidden * 2;
@@ -86,14 +89,23 @@ int routed_spans(const Routed& r, Span* s) {
   s[1] = {r.idx, slot_bytes};
   s[2] = {r.weights, slot_bytes};
   s[3] = {r.shared, r.shared ? r.tokens * row_bytes : 0};
-  s[4] = {r.err_flag, r.err_flag ? 4 : 0};
-  return 5;
+  s[kErrSpan] = {r.err_flag, r.err_flag ? 4 : 0};
+  return kErrSpan + 1;
 }
 
 bool overlaps_any(const void* p, int64_t n, const Span* s, int ns) {
   for (int i = 0; i < ns; ++i)
     if (overlap(p, n, s[i].p, s[i].bytes)) return true;
   return false;
+}
+
+// err_flag is written by the kernels, so it may not overlap anything they
+// read: every span of s (routed_spans() first, then any others) but its own.
+bool err_flag_clear(const Routed& r, const Span* s, int ns) {
+  if (r.err_flag == nullptr) return true;
+  for (int i = 0; i < ns; ++i)
+    if (i != kErrSpan && overlap(r.err_flag, 4, s[i].p, s[i].bytes)) return false;
+  return true;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOEF_OK : MOEF_ERR_HIP; }
@@ -160,6 +172,7 @@ int moe_finalize(const uint16_t* gemm2_out, int64_t num_rows,
   if (!aligned(out, 16)) return MOEF_ERR_MISALIGNED;
   Span s[8];
   const int ns = routed_spans(r, s);
+  if (!err_flag_clear(r, s, ns)) return MOEF_ERR_BAD_ALIAS;
   if (overlaps_any(out, num_tokens * hidden * 2, s, ns)) return MOEF_ERR_BAD_ALIAS;
   return hip_status(moef::launch_finalize(r, out, static_cast<hipStream_t>(stream)));
 }
@@ -196,6 +209,7 @@ int moe_finalize_residual_rmsnorm(const uint16_t* gemm2_out, int64_t num_rows,
   if (overlaps_any(residual_out, tb, s, ns)) return MOEF_ERR_BAD_ALIAS;
   if (residual_out != residual && overlap(residual_out, tb, residual, tb)) return MOEF_ERR_BAD_ALIAS;
   s[ns++] = {residual, tb};
+  if (!err_flag_clear(r, s, ns)) return MOEF_ERR_BAD_ALIAS;
   if (overlaps_any(normed, tb, s, ns) || overlap(normed, tb, residual_out, tb))
     return MOEF_ERR_BAD_ALIAS;
   return hip_status(moef::launch_finalize_rmsnorm(r, residual, gamma, eps, residual_out, normed,
@@ -225,6 +239,7 @@ int moe_finalize_quant_ue8m0(const uint16_t* gemm2_out, int64_t num_rows,
   const int64_t sb = num_tokens * (hidden / MOEF_QUANT_BLOCK);
   Span s[8];
   const int ns = routed_spans(r, s);
+  if (!err_flag_clear(r, s, ns)) return MOEF_ERR_BAD_ALIAS;
   if (overlaps_any(out_e4m3, qb, s, ns) || overlaps_any(scale_e8m0, sb, s, ns) ||
       overlap(out_e4m3, qb, scale_e8m0, sb))
     return MOEF_ERR_BAD_ALIAS;

@@ -67,7 +67,7 @@
  *    index and weight tensors 4-byte aligned. Else MOEF_ERR_MISALIGNED.
  *  - Aliasing: outputs may not overlap inputs or each other
  *    (MOEF_ERR_BAD_ALIAS), except that residual_out may be exactly residual
- *    (in-place residual update).
+ *    (in-place residual update). err_flag counts as an output.
  */
 #ifndef MOE_FINALIZE_H
 #define MOE_FINALIZE_H

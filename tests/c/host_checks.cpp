@@ -79,6 +79,17 @@ int main() {
                                                         at<float>(W), nullptr, nullptr, 1.0f,
                                                         at<uint16_t>(G2 + 16), 2, 8, 1, nullptr,
                                                         nullptr), MOEF_ERR_BAD_ALIAS, false);
+  check("finalize with a separate err_flag", moe_finalize(at<uint16_t>(G2), 8, at<int32_t>(IDX),
+                                                         at<float>(W), nullptr, nullptr, 1.0f,
+                                                         at<uint16_t>(OUT), 2, 8, 1,
+                                                         at<int32_t>(S), nullptr),
+        MOEF_OK, true);
+  check("finalize err_flag inside the index map", moe_finalize(at<uint16_t>(G2), 8,
+                                                               at<int32_t>(IDX), at<float>(W),
+                                                               nullptr, nullptr, 1.0f,
+                                                               at<uint16_t>(OUT), 2, 8, 1,
+                                                               at<int32_t>(IDX + 4), nullptr),
+        MOEF_ERR_BAD_ALIAS, false);
   // residual + RMSNorm
   check("rmsnorm ok", moe_finalize_residual_rmsnorm(
       at<uint16_t>(G2), 4096, at<int32_t>(IDX), at<float>(W), nullptr, at<uint16_t>(SH), 2.5f,

@@ -241,3 +241,16 @@ def test_allreduce_rules(lib):
     assert c(rk, 3, RES, GAM, 1e-6, RO, RO + tb - 16, T, H, None) == ALIAS
     assert c(rk, 3, RES, GAM, 1e-6, RO, GAM, T, H, None) == ALIAS
     assert c(rk, 3, RES, GAM, 1e-6, RO, G2 + 0x2_0000_0000, T, H, None) == ALIAS
+
+
+def test_err_flag_may_not_overlap_what_the_kernels_read(lib):
+    """err_flag is written by the kernels: inside gemm2_out, the index map, the
+    weights, the shared output, the residual or gamma it is an alias."""
+    for err in (G2 + 64, IDX, W + 8, SH + 4):
+        assert fin(lib, err=err) == ALIAS, hex(err)
+    r = lib.moe_finalize_residual_rmsnorm
+    for err in (RES + 4, GAM):
+        assert r(G2, 1024, IDX, W, None, SH, 2.5, RES, GAM, 1e-6, RO, NRM, 4, 4096, 8, err,
+                 None) == ALIAS
+    q = lib.moe_finalize_quant_ue8m0
+    assert q(G2, 1024, IDX, W, None, SH, 2.5, Q, S, 4, 4096, 8, IDX + 4, None) == ALIAS
