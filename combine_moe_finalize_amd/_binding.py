@@ -97,6 +97,14 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+def _code_bytes(t):
+    """E4M3 output as its bytes: a float8_e4m3fn tensor is written through a
+    uint8 view of the same memory (the caller gets its own tensor back)."""
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    return t
+
+
 def _tensor(t, name, dtype, shape):
     """dtype / shape / layout rule of one argument. The accepted case is one
     test; the messages are built only for a rejected argument."""
@@ -253,12 +261,11 @@ def moe_finalize_quant_ue8m0(gemm2_out: torch.Tensor,
         out_e4m3 = torch.empty((T, H), dtype=torch.uint8, device=device)
     if scale_e8m0 is None:
         scale_e8m0 = torch.empty((T, H // QUANT_BLOCK), dtype=torch.uint8, device=device)
-    if out_e4m3.dtype == torch.float8_e4m3fn:
-        out_e4m3 = out_e4m3.view(torch.uint8)
-    _dev_tensor(out_e4m3, "out_e4m3", torch.uint8, (T, H), device)
+    codes = _code_bytes(out_e4m3)
+    _dev_tensor(codes, "out_e4m3", torch.uint8, (T, H), device)
     _dev_tensor(scale_e8m0, "scale_e8m0", torch.uint8, (T, H // QUANT_BLOCK), device)
     _call("moe_finalize_quant_ue8m0", device, *args, float(routed_scaling_factor),
-          _ptr(out_e4m3), _ptr(scale_e8m0), T, H, K, _ptr(err_flag))
+          _ptr(codes), _ptr(scale_e8m0), T, H, K, _ptr(err_flag))
     return out_e4m3, scale_e8m0
 
 
@@ -323,14 +330,13 @@ def _act_quant(fn_name, x, out_e4m3, scale, scale_dtype):
     _tensor(x, "x", torch.bfloat16, (T, H))
     if out_e4m3 is None:
         out_e4m3 = torch.empty((T, H), dtype=torch.uint8, device=device)
-    if out_e4m3.dtype == torch.float8_e4m3fn:
-        out_e4m3 = out_e4m3.view(torch.uint8)
     if scale is None:
         scale = torch.empty((T, H // QUANT_BLOCK), dtype=scale_dtype, device=device)
-    _tensor(out_e4m3, "out_e4m3", torch.uint8, (T, H))
+    codes = _code_bytes(out_e4m3)
+    _tensor(codes, "out_e4m3", torch.uint8, (T, H))
     _tensor(scale, "scale", scale_dtype, (T, H // QUANT_BLOCK))
-    _on_device(device, x=x, out_e4m3=out_e4m3, scale=scale)
-    _call(fn_name, device, _ptr(x), T, H, _ptr(out_e4m3), _ptr(scale))
+    _on_device(device, x=x, out_e4m3=codes, scale=scale)
+    _call(fn_name, device, _ptr(x), T, H, _ptr(codes), _ptr(scale))
     return out_e4m3, scale
 
 

@@ -91,3 +91,11 @@ def test_cpu_tensors_are_rejected():
         B._on_device(t.device, x=t)
     with pytest.raises(ValueError, match="expected cuda:0"):
         B._on_device(torch.device("cuda:0"), x=t)
+
+
+def test_fp8_outputs_are_written_through_a_byte_view_and_returned_as_given():
+    f8 = torch.zeros((2, 128), dtype=torch.float8_e4m3fn)
+    codes = B._code_bytes(f8)
+    assert codes.dtype == torch.uint8 and codes.data_ptr() == f8.data_ptr()
+    u8 = torch.zeros((2, 128), dtype=torch.uint8)
+    assert B._code_bytes(u8) is u8

@@ -427,3 +427,24 @@ def test_graph_capture_replay():
         torch.cuda.synchronize()
         assert_bits_equal(h_bits(out), eager, f"graph replay {i}")
         _ = (torch.ones(1000, device=DEV) * i).sum().item()   # eager work between replays
+
+
+def test_float8_output_tensors():
+    """A float8_e4m3fn output is written through a byte view and returned as
+    the caller's own tensor; torch's decoding of the codes matches the
+    oracle's E4M3 decoding."""
+    wl = W.make_workload(8, 1024, 16, 4, rsf=2.5, seed=41)
+    announce("float8_e4m3fn outputs")
+    kw = device_inputs(wl)
+    q8 = torch.empty((wl.T, wl.H), dtype=torch.float8_e4m3fn, device=DEV)
+    got, s = M.moe_finalize_quant_ue8m0(**kw, out_e4m3=q8)
+    ref_q, ref_s = M.moe_finalize_quant_ue8m0(**kw)
+    xa = d_bf16(W.activations(8, 1024, seed=42))
+    a8 = torch.empty((8, 1024), dtype=torch.float8_e4m3fn, device=DEV)
+    got_a, _ = M.moe_act_quant_fp8_ue8m0(xa, out_e4m3=a8)
+    ref_a, _ = M.moe_act_quant_fp8_ue8m0(xa)
+    torch.cuda.synchronize()
+    assert got is q8 and got_a is a8
+    assert torch.equal(q8.view(torch.uint8), ref_q) and torch.equal(a8.view(torch.uint8), ref_a)
+    dec = q8.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(dec, F.e4m3_decode(ref_q.cpu().numpy()), equal_nan=True)
