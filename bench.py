@@ -170,28 +170,65 @@ def graph_us(torch, fn, n, reps=10):
 
 
 # --------------------------------------------------------------- CPU leg
-def cpu_baseline(wl, min_s=10.0, max_s=30.0, chunk=256):
+def e4m3_steps(a, b):
+    """Distance in E4M3 code steps between code arrays (sign-magnitude codes
+    mapped onto one ordered line; +0 and -0 coincide)."""
+    def line(c):
+        c = c.astype(np.int64)
+        m = c & 0x7F
+        return np.where(c & 0x80, -m, m)
+    return np.abs(line(a) - line(b))
+
+
+def cpu_baseline(wl, q_gpu=None, s_gpu=None, min_s=10.0, max_s=30.0, chunk=256,
+                 mirror_tokens=512):
     """The oracle (fp64 truth finalize + UE8M0 quant), single thread, in
     token chunks over the same workload, repeating passes until at least
-    min_s seconds of CPU work (stopping early at max_s)."""
+    min_s seconds of CPU work (stopping early at max_s).
+
+    With the GPU's codes and scale bytes given, the first pass's oracle
+    outputs are also compared with them after the timing: against the fp64
+    truth over every token (scale bytes equal, codes within one step), and
+    against the oracle's fp32 mirror of the kernels' operation order, untimed,
+    on the first mirror_tokens tokens (bit-exact)."""
     from oracle import finalize as O
+    keep = q_gpu is not None
+    t_codes = np.empty((wl.T, wl.H), np.uint8) if keep else None
+    t_scales = np.empty((wl.T, wl.H // 128), np.uint8) if keep else None
     done = 0
     t0 = time.perf_counter()
     while True:
         start = done % wl.T
         sl = slice(start, min(wl.T, start + chunk))
-        O.finalize_quant_truth(wl.gemm2_out, wl.idx[sl], weights_f32=wl.weights[sl],
-                               shared=wl.shared[sl], rsf=wl.rsf)
+        qc, sc, _ = O.finalize_quant_truth(wl.gemm2_out, wl.idx[sl], weights_f32=wl.weights[sl],
+                                           shared=wl.shared[sl], rsf=wl.rsf)
+        if keep and done < wl.T:
+            t_codes[sl], t_scales[sl] = qc, sc
         done += sl.stop - sl.start
         el = time.perf_counter() - t0
         if (el >= min_s and done % wl.T == 0) or el >= max_s:
             break
     dt = time.perf_counter() - t0
     gbs = bytes_quant(done, wl.H, wl.top_k) / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    base = {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} tokens ({done / wl.T:.2f} passes over the T={wl.T} workload) "
                       f"through the fp64 finalize + UE8M0/E4M3 quant oracle, numpy, one "
                       f"thread, {dt:.1f} s"}
+    if not keep:
+        return base, None
+    n = min(done, wl.T)
+    steps = e4m3_steps(q_gpu[:n], t_codes[:n])
+    m = min(mirror_tokens, wl.T)
+    mq, ms, _ = O.finalize_quant_mirror(wl.gemm2_out, wl.idx[:m], weights_f32=wl.weights[:m],
+                                        shared=wl.shared[:m], rsf=wl.rsf)
+    parity = {"tokens_vs_fp64_truth": int(n),
+              "scale_bytes_differing_vs_truth": int(np.count_nonzero(s_gpu[:n] != t_scales[:n])),
+              "max_code_steps_vs_truth": int(steps.max()) if steps.size else 0,
+              "codes_differing_vs_truth": int(np.count_nonzero(steps)),
+              "tokens_vs_fp32_mirror": int(m),
+              "code_mismatches_vs_mirror": int(np.count_nonzero(q_gpu[:m] != mq)),
+              "scale_mismatches_vs_mirror": int(np.count_nonzero(s_gpu[:m] != ms))}
+    return base, parity
 
 
 # ----------------------------------------------------------------- sweep
@@ -406,6 +443,9 @@ def main():
                                          f"timed launches, divided by {args.steps}",
                      "algorithmic_bytes_per_launch": nbytes},
     }
+    # the timed launches' outputs, kept on the host for the CPU leg's parity report
+    q_host = q.cpu().numpy() if not args.no_cpu_baseline else None
+    s_host = s.cpu().numpy() if not args.no_cpu_baseline else None
     del kw, q, s
     torch.cuda.empty_cache()
     if not args.no_sweep:
@@ -419,7 +459,7 @@ def main():
                                  per_call}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(wl, q_host, s_host)
     print(json.dumps(result), flush=True)
 
 

@@ -91,3 +91,28 @@ def test_committed_counters_match_the_committed_source():
     assert c["kernel_source_sha256"] == bench.kernel_source_hash()
     assert c["algorithmic_bytes_per_launch"] == bench.bytes_quant(8192, 7168, 8)
     assert 1.0 <= c["traffic_over_algorithmic"] < 1.05
+
+
+def test_parity_statistics_of_the_cpu_leg():
+    """The CPU leg's parity report: outputs equal to the oracle's fp32 mirror
+    show no mismatch; one flipped code is counted against both references."""
+    from oracle import finalize as O
+    wl = W.make_workload(40, 1024, 16, 8, rsf=2.5, seed=3, log2_mag=(-8.0, 8.0))
+    q, s, _ = O.finalize_quant_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                                      shared=wl.shared, rsf=wl.rsf)
+    base, par = bench.cpu_baseline(wl, q, s, min_s=0.0, max_s=60.0, chunk=16, mirror_tokens=24)
+    assert base["kind"] == "oracle" and base["cores"] == 1
+    assert par["tokens_vs_fp64_truth"] == 40 and par["tokens_vs_fp32_mirror"] == 24
+    assert par["code_mismatches_vs_mirror"] == 0 and par["scale_mismatches_vs_mirror"] == 0
+    assert par["max_code_steps_vs_truth"] <= 1
+    q2 = q.copy()
+    q2[3, 5] = q2[3, 5] ^ 0x04                     # four steps away
+    _, par2 = bench.cpu_baseline(wl, q2, s, min_s=0.0, max_s=60.0, chunk=16, mirror_tokens=24)
+    assert par2["code_mismatches_vs_mirror"] == 1
+    assert par2["max_code_steps_vs_truth"] >= 3
+
+
+def test_e4m3_step_distance():
+    a = np.array([0x00, 0x80, 0x01, 0x81, 0x7E, 0x38], np.uint8)
+    b = np.array([0x80, 0x00, 0x81, 0x01, 0x7D, 0x3A], np.uint8)
+    assert bench.e4m3_steps(a, b).tolist() == [0, 0, 2, 2, 1, 2]
