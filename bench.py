@@ -443,6 +443,27 @@ def main():
                                          f"timed launches, divided by {args.steps}",
                      "algorithmic_bytes_per_launch": nbytes},
     }
+    # us/call of the same operation on the first T tokens of the same workload,
+    # T = 1, 2, 4, ..., 8192, per call under HIP-graph replay
+    curve = {}
+    if not args.no_sweep:
+        idx_all, w_all, sh_all = (kw["expanded_idx_to_permuted_idx"], kw["topk_weights"],
+                                  kw["shared_out"])
+        Tc = 1
+        while Tc <= T:
+            kc = dict(kw, expanded_idx_to_permuted_idx=idx_all[:Tc], topk_weights=w_all[:Tc],
+                      shared_out=sh_all[:Tc])
+            qc, sc = q[:Tc], s[:Tc]
+            us = graph_us(torch, lambda: M.moe_finalize_quant_ue8m0(**kc, out_e4m3=qc,
+                                                                     scale_e8m0=sc),
+                          n=20 if Tc <= 256 else 5, reps=5 if Tc <= 1024 else 2)
+            gbs = bytes_quant(Tc, H, k) / us / 1e3
+            curve[str(Tc)] = {"us": round(us, 3), "gbs": round(gbs, 1),
+                              "frac": round(gbs / HBM_PEAK_GBS, 4)}
+            log(f"prefill op T={Tc}: {us:.3f} us/call, {gbs:.0f} GB/s")
+            Tc *= 2
+        step()                                   # the timed launches' outputs again
+        torch.cuda.synchronize()
     # the timed launches' outputs, kept on the host for the CPU leg's parity report
     q_host = q.cpu().numpy() if not args.no_cpu_baseline else None
     s_host = s.cpu().numpy() if not args.no_cpu_baseline else None
@@ -454,9 +475,9 @@ def main():
         # under HIP-graph replay, and the timed prefill launch (T=8192)
         per_call = {str(r["T"]): r["us_graph_replay"] for r in result["sweep"]
                     if r["case"] == "decode"}
-        per_call["8192"] = round(avg_us, 3)
-        result["us_per_call"] = {"decode_finalize_H4096_k8_graph_replay_and_prefill_T8192":
-                                 per_call}
+        result["us_per_call"] = {
+            "finalize_quant_ue8m0_H7168_k8_graph_replay": curve,
+            "finalize_H4096_k8_graph_replay": per_call}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"], result["parity"] = cpu_baseline(wl, q_host, s_host)
