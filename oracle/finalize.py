@@ -99,10 +99,19 @@ def slot_validity(idx, num_rows):
     return valid, flag
 
 
+def _rows_or_zero(gemm2_out):
+    """gemm2_out itself, or one zero row when it has none (a rank holding no
+    expert of the batch): every slot is then skipped, and the row stands in
+    only so that the skipped slots have something to index."""
+    if gemm2_out.shape[0] > 0:
+        return gemm2_out
+    return np.zeros((1, gemm2_out.shape[1]), dtype=gemm2_out.dtype)
+
+
 def _gather(gemm2_out, idx, valid):
     """float64 rows x[perm[t,k], :] for valid slots, 0 for skipped ones."""
     safe = np.where(valid, idx, 0)
-    x = F.bf16_to_f64(gemm2_out[safe])            # [T, k, H]
+    x = F.bf16_to_f64(_rows_or_zero(gemm2_out)[safe])   # [T, k, H]
     x[~valid] = 0.0
     return x
 
@@ -147,7 +156,7 @@ def finalize_mirror_f32(gemm2_out, idx, weights_f32=None, packed=None,
     acc = np.zeros((T, H), dtype=np.float32)
     for k in range(K):
         rows = np.where(valid[:, k], idx[:, k], 0)
-        x = F.bf16_to_f32(gemm2_out[rows])                 # [T, H]
+        x = F.bf16_to_f32(_rows_or_zero(gemm2_out)[rows])  # [T, H]
         prod = w[:, k, None] * x                            # fp32 multiply
         acc = np.where(valid[:, k, None], acc + prod, acc)  # fp32 add
     if shared is not None:

@@ -283,6 +283,32 @@ def test_index_rules_skip_and_flag():
     assert flag == 0
 
 
+def test_rank_with_no_rows():
+    """A rank that holds none of the batch's experts has no gemm2_out rows:
+    every slot is -1, so the finalize is the shared output alone (zeros
+    without one), and any index >= 0 is past the end and flagged."""
+    T, H, K = 4, 256, 3
+    rng = np.random.default_rng(8)
+    g2 = np.zeros((0, H), np.uint16)
+    sh = W.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    res = W.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    idx = np.full((T, K), -1, np.int32)
+    w = rng.random((T, K)).astype(np.float32)
+    for mode in (O.finalize_truth, O.finalize_mirror):
+        out, flag = mode(g2, idx, weights_f32=w, shared=sh, rsf=2.5)
+        assert flag == 0 and np.array_equal(out, sh)
+        out, flag = mode(g2, idx, weights_f32=w, rsf=2.5)
+        assert flag == 0 and not out.any()
+    ro, _, flag = O.finalize_residual_rmsnorm_mirror(g2, idx, residual=res, gamma=res[0],
+                                                     eps=1e-6, weights_f32=w, shared=sh)
+    exact = F.bf16_to_f64(sh) + F.bf16_to_f64(res)   # exact in fp64: two bf16 values
+    assert flag == 0 and np.array_equal(ro, F.bf16_bits(exact))
+    idx[1, 2] = 0
+    for mode in (O.finalize_truth, O.finalize_mirror):
+        out, flag = mode(g2, idx, weights_f32=w, shared=sh, rsf=2.5)
+        assert flag == O.ERR_INDEX_OUT_OF_RANGE and np.array_equal(out, sh)
+
+
 def test_mirror_within_two_ulp_of_truth():
     wl = W.config_workload(1, 64)
     m, _ = O.finalize_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
