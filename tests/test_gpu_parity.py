@@ -16,7 +16,8 @@ from oracle import finalize as O
 from oracle import formats as F
 
 from gpu_helpers import (DEV, abs_terms, announce, assert_bf16_within_tolerance,
-                         assert_bits_equal, d_bf16, d_f32, d_i32, device_inputs, h_bits, h_u8)
+                         assert_bits_equal, d_bf16, d_f32, d_i32, device_inputs, h_bits, h_u8,
+                         ulp_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -448,3 +449,54 @@ def test_float8_output_tensors():
     assert torch.equal(q8.view(torch.uint8), ref_q) and torch.equal(a8.view(torch.uint8), ref_a)
     dec = q8.float().cpu().numpy().astype(np.float64)
     assert np.array_equal(dec, F.e4m3_decode(ref_q.cpu().numpy()), equal_nan=True)
+
+
+def test_rank_with_no_rows():
+    """An expert-parallel rank that holds none of the batch's experts: no
+    gemm2_out rows (num_rows 0) and every slot -1. Each routed entry point
+    returns what the oracle gives for the shared output alone, and an index
+    >= 0 is skipped and flagged. The C call also takes a NULL gemm2_out."""
+    T, H, K = 5, 1024, 4
+    rng = np.random.default_rng(17)
+    g2 = np.zeros((0, H), np.uint16)
+    sh = W.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    res = W.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    gam = W.to_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32))
+    w = rng.random((T, K)).astype(np.float32)
+    for stray in (False, True):
+        idx = np.full((T, K), -1, np.int32)
+        if stray:
+            idx[2, 1] = 0                                  # row 0 does not exist here
+        announce(f"rank with no rows, stray index {stray}")
+        kw = dict(topk_weights=d_f32(w), shared_out=d_bf16(sh), routed_scaling_factor=2.5)
+        errs = [torch.zeros(1, dtype=torch.int32, device=DEV) for _ in range(3)]
+        d_g2, d_idx = d_bf16(g2), d_i32(idx)
+        out = M.moe_finalize(d_g2, d_idx, err_flag=errs[0], **kw)
+        ro, nm = M.moe_finalize_residual_rmsnorm(d_g2, d_idx, residual=d_bf16(res),
+                                                 gamma=d_bf16(gam), eps=1e-6, err_flag=errs[1],
+                                                 **kw)
+        q, sc = M.moe_finalize_quant_ue8m0(d_g2, d_idx, err_flag=errs[2], **kw)
+        torch.cuda.synchronize()
+        okw = dict(weights_f32=w, shared=sh, rsf=2.5)
+        m_out, flag = O.finalize_mirror(g2, idx, **okw)
+        assert_bits_equal(h_bits(out), m_out, "finalize")
+        m_ro, m_nm, _ = O.finalize_residual_rmsnorm_mirror(g2, idx, residual=res, gamma=gam,
+                                                           eps=1e-6, **okw)
+        assert_bits_equal(h_bits(ro), m_ro, "residual_out")
+        g, o = F.bf16_to_f64(h_bits(nm)), F.bf16_to_f64(m_nm)
+        assert np.all(np.abs(g - o) <= ulp_bf16(o)), "normed"
+        m_q, m_s, _ = O.finalize_quant_mirror(g2, idx, **okw)
+        assert_bits_equal(sc.cpu().numpy(), m_s, "scales")
+        assert_bits_equal(q.cpu().numpy(), m_q, "codes")
+        assert flag == (M.DEVERR_INDEX_OUT_OF_RANGE if stray else 0)
+        assert [int(e.item()) for e in errs] == [flag] * 3
+    L = M.load_library()
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    d_idx = d_i32(np.full((T, K), -1, np.int32))
+    d_w, err = d_f32(w), torch.zeros(1, dtype=torch.int32, device=DEV)
+    announce("rank with no rows, NULL gemm2_out and no shared output")
+    assert L.moe_finalize(None, 0, d_idx.data_ptr(), d_w.data_ptr(), None, None, 2.5,
+                          out.data_ptr(), T, H, K, err.data_ptr(),
+                          torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert not h_bits(out).any() and int(err.item()) == 0     # +0 everywhere
