@@ -19,8 +19,11 @@
 // processor", IBM J. Res. Dev. 34(1), 1990). The result is bit-identical to
 // the IEEE quotient whenever the operands and residuals are normal fp32
 // numbers. Outside that, |x| < 2^-100 with s >= 2^-60, so both quotients are
-// below 2^-40 and encode to the same signed zero. Blocks whose scale falls
-// outside [2^-60, 2^60] keep the IEEE division.
+// below 2^-40 and encode to the same signed zero. The scale itself,
+// fl(amax / 448), takes the same sequence with the constant fl(1/448). Blocks
+// whose scale falls outside [2^-60, 2^60] keep the IEEE divisions. Each code
+// takes its sign from its input (one byte permute per four codes), which
+// also restores the sign of a zero quotient.
 //
 // The input is read as a flat run of 16-byte vectors (8 bf16 each). Since
 // hidden is a multiple of 128, every aligned group of 16 vectors is one
@@ -47,13 +50,35 @@ using namespace dev;
 //  * one residual step makes q2 faithful (within 1 ulp);
 //  * with y within half an ulp of 1/s and q2 faithful, the residual
 //    x - s q2 is exact and fl(q2 + (x - s q2) y) = fl(x/s) (Markstein).
-// copysign restores the sign of a zero quotient, which a cancelling final sum
-// would make +0.
+// A zero quotient of a negative x may come out as +0 (a cancelling final
+// sum); the caller takes the signs from the inputs.
 __device__ __forceinline__ float div_rn(float x, float s, float y) {
   const float q1 = x * y;
   const float q2 = __builtin_fmaf(__builtin_fmaf(-s, q1, x), y, q1);
-  const float q3 = __builtin_fmaf(__builtin_fmaf(-s, q2, x), y, q2);
-  return __builtin_copysignf(q3, x);
+  return __builtin_fmaf(__builtin_fmaf(-s, q2, x), y, q2);
+}
+
+// bf16 bits of the block maxima 1.75 * 2^-52 and 1.75 * 2^68, between which
+// s = amax / 448 lies in [2^-60, 2^60].
+constexpr uint32_t kAmaxDivLo = (75u << 7) | 0x60u;
+constexpr uint32_t kAmaxDivHi = (195u << 7) | 0x60u;
+// fl(1 / 448), the reciprocal div_rn takes for the scale.
+constexpr float kRcp448 = 1.0f / 448.0f;
+
+// Eight fp32 values -> eight E4M3 codes, nearest even (the plain converter),
+// two per op, in column order.
+__device__ __forceinline__ u32x2 e4m3x8(const float f[8]) {
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+  return u32x2{(uint32_t)lo, (uint32_t)hi};
+}
+
+// The sign bits of the four bf16 values in (a, b), as bit 7 of bytes 0..3
+// (byte j holds the code of value j: a's low and high halves, then b's).
+__device__ __forceinline__ uint32_t signs4(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07050301u) & 0x80808080u;
 }
 
 // Quantizes one lane's 8 values (vector vi of the flat [T, H/8] view); the
@@ -70,23 +95,23 @@ __device__ __forceinline__ void quant_vector(const u32x4 v, bool active, int64_t
     q = e4m3x8_scaled(v, ue8m0_scale(ex));
     if (active && (lane & 15) == 0) scale_e8m0[vi >> 4] = (uint8_t)(ex + 127);
   } else {
-    const float a = __uint_as_float(amax << 16);
-    const float s = a > 0.0f ? a / 448.0f : 1.0f;
     float f[8];
     unpack8(v, f);
-    if (s >= 0x1p-60f && s <= 0x1p60f) {        // block-uniform: whole 16-lane rows
+    float s;
+    if (amax >= kAmaxDivLo && amax <= kAmaxDivHi) {    // block-uniform: whole 16-lane rows
+      s = div_rn(__uint_as_float(amax << 16), 448.0f, kRcp448);
       const float y = 1.0f / s;
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = div_rn(f[e], s, y);
     } else {
+      const float a = __uint_as_float(amax << 16);
+      s = a > 0.0f ? a / 448.0f : 1.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = f[e] / s;
     }
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
-    q = u32x2{(uint32_t)lo, (uint32_t)hi};
+    q = e4m3x8(f);
+    q.x |= signs4(v.x, v.y);
+    q.y |= signs4(v.z, v.w);
     if (active && (lane & 15) == 0) scale_f32[vi >> 4] = s;
   }
   if (active) __builtin_nontemporal_store(q, out_q + vi);
