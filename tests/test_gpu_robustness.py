@@ -1,5 +1,5 @@
 """Robustness of every entry point on the GPU: HIP-graph capture and replay,
-run-to-run determinism, guard canaries around every output, the maximum
+launch on the caller's stream, run-to-run determinism, guard canaries around every output, the maximum
 hidden size and an odd large token count. Expected values come from the
 oracle or from the same call run eagerly (replay and determinism checks)."""
 import numpy as np
@@ -151,6 +151,31 @@ def test_graph_capture_replay_every_entry_point():
             _ = (torch.arange(4096, device=DEV) * i).sum().item()   # eager work between replays
         assert all(canaries_intact(b) for b in bufs), name
         del g
+
+
+def test_calls_run_on_the_callers_stream():
+    """Every entry point launches on the stream current at the call. A side
+    stream runs a few milliseconds of fills, then overwrites the outputs with
+    a pattern, then makes the call: only a launch queued on that stream,
+    behind the pattern, leaves the eager result in the outputs."""
+    busy = torch.empty(1 << 28, dtype=torch.int32, device=DEV)          # 1 GiB
+    for name, fn, outs, bufs in entry_points():
+        announce(f"caller's stream: {name}")
+        fn()
+        torch.cuda.synchronize()
+        eager = snapshot(outs)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(8):
+                busy.fill_(i)
+            for t in outs:
+                t.view(torch.uint8).fill_(0x3C) if t.dtype != torch.uint8 else t.fill_(0x3C)
+            fn()
+        torch.cuda.synchronize()
+        assert same(eager, outs), f"{name}: the call did not run behind its stream's work"
+        assert all(canaries_intact(b) for b in bufs), name
+    del busy
 
 
 def test_maximum_hidden_size():
