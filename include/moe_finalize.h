@@ -61,7 +61,9 @@
  *    slot k in ascending order acc = acc + w'_k * x_k (separate fp32 multiply
  *    and add, no fused multiply-add); acc = acc + shared; [acc = acc +
  *    residual]; one round-to-nearest-even to bf16. The routed scaling factor
- *    never scales the shared-expert output.
+ *    never scales the shared-expert output. Non-finite values propagate
+ *    through that arithmetic (an fp32 overflow of the sum gives inf); the
+ *    sign of a NaN the arithmetic creates (inf - inf) is not specified.
  *  - Alignment: bf16 row tensors (gemm2_out, shared_out, out, residual,
  *    residual_out, normed, gamma) 16-byte aligned; FP8 output 8-byte aligned;
  *    index and weight tensors 4-byte aligned. Else MOEF_ERR_MISALIGNED.
@@ -140,7 +142,8 @@ int moe_finalize(const uint16_t* gemm2_out, int64_t num_rows,
  *                rounding; may be exactly `residual` (in place).
  *  normed        bf16 [num_tokens, hidden] =
  *                bf16(ro / sqrt(mean_h(ro^2) + eps) * gamma), ro being the
- *                stored bf16 residual_out, computed in fp32.
+ *                stored bf16 residual_out, computed in fp32; not
+ *                specified for a token whose residual_out holds inf or NaN.
  *  hidden        at most MOEF_MAX_HIDDEN_RMSNORM.
  */
 int moe_finalize_residual_rmsnorm(const uint16_t* gemm2_out, int64_t num_rows,
@@ -165,6 +168,9 @@ int moe_finalize_residual_rmsnorm(const uint16_t* gemm2_out, int64_t num_rows,
  *  scale_e8m0  uint8 [num_tokens, hidden / 128], the byte e + 127 where e is
  *              the least integer with max|y over the block| <= 448 * 2^e,
  *              clamped to [-127, 127] (an all-zero block gives e = -127).
+ *              A block where y holds inf or NaN gets e = 127; its finite
+ *              values encode as above and each non-finite one gets an E4M3
+ *              NaN code (0x7F or 0xFF, the sign not specified).
  *  hidden      a multiple of 128.
  */
 int moe_finalize_quant_ue8m0(const uint16_t* gemm2_out, int64_t num_rows,

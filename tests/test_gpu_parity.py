@@ -500,3 +500,61 @@ def test_rank_with_no_rows():
                           torch.cuda.current_stream().cuda_stream) == 0
     torch.cuda.synchronize()
     assert not h_bits(out).any() and int(err.item()) == 0     # +0 everywhere
+
+
+def test_non_finite_values():
+    """Non-finite results follow the fp32 arithmetic of the definition:
+    +inf and -inf rows in one token give NaN, one +inf gives +inf, bf16-max
+    rows whose weighted sum passes the fp32 range give +inf, a NaN row gives
+    NaN. A generated NaN's sign is the platform's (x86 and gfx950 differ), so
+    NaNs are compared as NaN and every other element bit for bit. In the
+    quant epilogue a block holding a non-finite value takes e = 127 (the
+    clamp), its finite values encode exactly, and each non-finite value gets
+    an E4M3 NaN code. residual_out follows the same rule; normed is checked
+    on the tokens whose residual_out is finite."""
+    wl = W.make_workload(4, 256, 8, 4, rsf=2.5, seed=5, pad=8, with_residual=True)
+    g2, r = wl.gemm2_out.copy(), wl.idx
+    g2[r[0, 0], 3], g2[r[0, 1], 3] = 0x7F80, 0xFF80      # +inf, -inf -> NaN
+    g2[r[0, 2], 4] = 0x7F80                              # +inf
+    for k in range(4):
+        g2[r[1, k], 5] = 0x7F7F                          # bf16 max: fp32 overflow
+    g2[r[2, 3], 6] = 0x7FC0                              # NaN
+    w = wl.weights.copy()
+    w[1, :] = 0.25
+    wl.gemm2_out, wl.weights = g2, w
+    kw = device_inputs(wl)
+    announce("non-finite values")
+    out = M.moe_finalize(**kw)
+    q, s = M.moe_finalize_quant_ue8m0(**kw)
+    ro, nm = M.moe_finalize_residual_rmsnorm(**kw, residual=d_bf16(wl.residual),
+                                             gamma=d_bf16(wl.gamma), eps=wl.eps)
+    torch.cuda.synchronize()
+    okw = dict(weights_f32=w, shared=wl.shared, rsf=wl.rsf)
+    with np.errstate(over="ignore", invalid="ignore"):
+        m_out, _ = O.finalize_mirror(g2, r, **okw)
+        m_q, m_s, _ = O.finalize_quant_mirror(g2, r, **okw)
+        m_ro, m_nm, _ = O.finalize_residual_rmsnorm_mirror(
+            g2, r, residual=wl.residual, gamma=wl.gamma, eps=wl.eps, **okw)
+
+    def nan_aware(got, want, what):
+        gn = np.isnan(F.bf16_to_f64(got))
+        wn = np.isnan(F.bf16_to_f64(want))
+        assert np.array_equal(gn, wn), f"{what}: NaN positions differ"
+        assert_bits_equal(got[~wn], want[~wn], what)
+
+    got = h_bits(out)
+    nan_aware(got, m_out, "finalize")
+    assert got[0, 4] == 0x7F80 and got[1, 5] == 0x7F80
+    assert np.isnan(F.bf16_to_f64(got[[0, 2], [3, 6]])).all()
+    y = F.bf16_to_f64(m_out)
+    bad = ~np.isfinite(y)
+    assert_bits_equal(h_u8(s), m_s, "scales")
+    assert (h_u8(s)[[0, 1, 2], 0] == 254).all()
+    gq = h_u8(q)
+    assert_bits_equal(gq[~bad], m_q[~bad], "codes of finite values")
+    assert np.isin(gq[bad], [0x7F, 0xFF]).all(), "non-finite values need a NaN code"
+    nan_aware(h_bits(ro), m_ro, "residual_out")
+    fin = np.isfinite(F.bf16_to_f64(m_ro)).all(axis=1)
+    assert fin.tolist() == [False, False, False, True]
+    g, o = F.bf16_to_f64(h_bits(nm)[fin]), F.bf16_to_f64(m_nm[fin])
+    assert np.all(np.abs(g - o) <= ulp_bf16(o)), "normed of the finite token"
