@@ -16,9 +16,10 @@ are given here so they can be compared:
     rounded fp32 division, then one nearest-even rounding to E4M3); the scale
     is returned as float32.
 
-Readings: the block is 1 x 128 along the hidden dimension (the workload's
-block); inputs are finite bf16 (a NaN or inf input makes its block's codes
-unspecified).
+Readings: Q1 the block is 1 x 128 along the
+hidden dimension (the workload's block); Q2, Q3 the continuous scale and
+codes as above; Q4 inputs are finite bf16 (a NaN or inf input makes its
+block's codes unspecified).
 """
 from __future__ import annotations
 

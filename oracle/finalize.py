@@ -25,19 +25,24 @@ What is computed (plain definition, written from the pages):
 * Power-of-two (UE8M0) FP8 activation scales ("[FP8][MoE] Honor UE8M0
   activation scales in Triton MoE", Motivation and "More context").
 
-Readings taken where the pages are silent:
-  R1  out[t,h] = bf16( sum_k w'[t,k] * x[perm[t,k], h] + shared[t,h] ),
-      w' = fp32(w * rsf); rsf scales routed experts only, never shared.
-  R2  one rounding to bf16 (nearest-even) at the very end.
-  R3  perm is token-major [T, top_k]; perm < 0 skips the slot (expert not
-      local); perm >= P skips the slot and sets bit 0 of the error flag.
-  R4  shared_out may be absent (zeros).
-  R5  residual_out = bf16(finalize_acc + residual) (one rounding);
-      normed = bf16(ro / sqrt(mean(ro^2) + eps) * gamma) on the stored bf16
-      residual_out.
-  R6  quant input is the bf16-rounded finalize result y; per 1x128 block
-      e = least integer with amax <= 448 * 2^e (clamp [-127, 127], amax 0
-      gives -127), q = e4m3(y * 2^-e), scale byte e + 127.
+Readings taken where the pages are silent (R1, the fp32 operation order, is
+the mirror mode below):
+  R2, R3   out[t,h] = bf16( sum_k w'[t,k] * x[perm[t,k], h] + shared[t,h] ),
+           w' = fp32(w * rsf); rsf scales routed experts only, never shared;
+           shared is added into the accumulator before the rounding.
+  R4       one rounding to bf16 (nearest even) at the very end.
+  R5, R6   perm is token-major [T, top_k]; perm < 0 skips the slot (expert
+           not local); perm >= P skips the slot and sets bit 0 of the error
+           flag; P = 0 (no rows here) is allowed.
+  R7       shared_out may be absent (zeros).
+  R11, R12 residual_out = bf16(finalize_acc + residual) (one rounding);
+           normed = bf16(ro / sqrt(mean(ro^2) + eps) * gamma) on the stored
+           bf16 residual_out.
+  R13-R18  OCP E4M3 (max 448); the quant input is the bf16-rounded finalize
+           result y; per 1x128 block e = least integer with
+           amax <= 448 * 2^e (clamp [-127, 127], amax 0 gives -127),
+           q = e4m3(y * 2^-e) with ties to even and the sign of zero kept,
+           scale byte e + 127, row-major [T, H/128].
 
 Two modes:
   * ``*_truth``: fp64 gather, products and sums (each product w' * x is
@@ -92,7 +97,7 @@ def effective_weights(weights_f32, packed, rsf):
 
 
 def slot_validity(idx, num_rows):
-    """Reading R3: which (t, k) slots are gathered, and the error flag."""
+    """Readings R5, R6: which (t, k) slots are gathered, and the error flag."""
     idx = np.asarray(idx, dtype=np.int64)
     valid = (idx >= 0) & (idx < num_rows)
     flag = ERR_INDEX_OUT_OF_RANGE if np.any(idx >= num_rows) else 0
@@ -120,7 +125,7 @@ def _gather(gemm2_out, idx, valid):
 
 def finalize_truth_f64(gemm2_out, idx, weights_f32=None, packed=None,
                        shared=None, rsf=1.0):
-    """fp64 finalize accumulator [T, H] before rounding (readings R1-R4),
+    """fp64 finalize accumulator [T, H] before rounding (readings R2-R7),
     and the error flag. ``gemm2_out`` is uint16 bf16 bits [P, H]."""
     gemm2_out = np.asarray(gemm2_out, dtype=np.uint16)
     idx = np.asarray(idx)
@@ -178,7 +183,7 @@ def finalize_mirror(gemm2_out, idx, weights_f32=None, packed=None,
 
 def rmsnorm_f64(x_bits, gamma_bits, eps):
     """RMSNorm of bf16 rows in fp64, rounded once to bf16:
-    y = x / sqrt(mean(x^2) + eps) * gamma (reading R5)."""
+    y = x / sqrt(mean(x^2) + eps) * gamma (reading R11)."""
     x = F.bf16_to_f64(x_bits)
     g = F.bf16_to_f64(gamma_bits)
     ms = np.mean(x * x, axis=-1, keepdims=True)
@@ -189,7 +194,7 @@ def rmsnorm_f64(x_bits, gamma_bits, eps):
 def finalize_residual_rmsnorm_truth(gemm2_out, idx, weights_f32=None,
                                     packed=None, shared=None, rsf=1.0,
                                     residual=None, gamma=None, eps=1e-6):
-    """(residual_out bits, normed bits, flag) with fp64 math (reading R5).
+    """(residual_out bits, normed bits, flag) with fp64 math (readings R11, R12).
     ("[Kimi K2.5] Fuse deferred MoE finalize into next-layer AR + residual +
     RMSNorm", Summary: combine + shared add + residual + RMSNorm, keeping
     residual_out.)"""
@@ -214,7 +219,7 @@ def finalize_residual_rmsnorm_mirror(gemm2_out, idx, weights_f32=None,
 
 def quant_ue8m0(y_bits, block=QUANT_BLOCK):
     """Quantize bf16 rows [T, H] to OCP E4M3 codes [T, H] with one
-    power-of-two scale per 1 x ``block`` block along H (reading R6).
+    power-of-two scale per 1 x ``block`` block along H (readings R13-R18).
     Returns (codes uint8 [T, H], scale bytes uint8 [T, H/block],
     exponents int64 [T, H/block])."""
     y = F.bf16_to_f64(y_bits)
@@ -301,7 +306,7 @@ def ep_combine_truth(partials, shared=None):
 #        the sum is rounded once to bf16: that is residual_out;
 #   AR2  the shared-expert output is already inside the ranks' outputs (each
 #        rank's finalize adds its own share), so it is not a separate input;
-#   AR3  normed is the RMSNorm of the stored bf16 residual_out (reading R5).
+#   AR3  normed is the RMSNorm of the stored bf16 residual_out (reading R11).
 # ------------------------------------------------------------------------
 
 def allreduce_residual_rmsnorm_mirror(partials, residual, gamma, eps=1e-6):
