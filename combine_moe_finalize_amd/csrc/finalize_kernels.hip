@@ -25,8 +25,11 @@
 //
 // Epilogues:
 //  * RMSNorm: one workgroup per token (up to 16 waves), the row stays in
-//    registers; sum of squares by cross-lane shuffles in the wave, then LDS
-//    across waves, summed in a fixed order so every lane sees the same value.
+//    registers; the sum of squares of each 512-column chunk by cross-lane
+//    shuffles, then the chunk sums through LDS in chunk order, so every lane
+//    sees the same value and the result does not depend on the workgroup
+//    width. From 1024 tokens on, a token takes half as many waves with two
+//    column vectors per lane (measured faster there, slower below).
 //  * UE8M0 quant: a 1 x 128 block is 16 lanes x 8 columns, one DPP row; its
 //    absolute maximum is taken on bf16 bit patterns (packed 16-bit integer
 //    max, then four DPP row rotations), the power-of-two exponent comes from
@@ -180,11 +183,14 @@ __global__ void __launch_bounds__(kNormMaxThreads)
 finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __restrict__ gamma,
                         float eps, float inv_hidden, u32x4* residual_out,
                         u32x4* __restrict__ normed) {
-  __shared__ float partial[kNormMaxThreads / kWaveLanes];
+  // One partial sum of squares per 512-column chunk, summed in chunk order:
+  // the result does not depend on how many waves share the row.
+  __shared__ float partial[kNormMaxChunks];
   const int t = blockIdx.x;
   const int nthreads = blockDim.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int nw = nthreads >> 6;
 
   const u32x4* res_row = residual + (int64_t)t * a.h8;
   // row-independent operands first: shared, residual and gamma vectors
@@ -202,7 +208,6 @@ finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __rest
   load_route<KMAX, EXACT>(a, t, row, w);
 
   float ro[CPT][8];
-  float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int colv = threadIdx.x + i * nthreads;
@@ -212,18 +217,18 @@ finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __rest
     finalize_acc<KMAX, EXACT>(a, col, row, w, d[i], true, acc);
     const u32x4 rb = pack8_rne(acc);
     unpack8(rb, ro[i]);                     // the stored bf16 residual_out
+    float ss = 0.0f;
     if (active) {
       __builtin_nontemporal_store(rb, residual_out + (int64_t)t * a.h8 + colv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = ss + ro[i][e] * ro[i][e];
     }
+    ss = wave_sum(ss);
+    if (lane == 0) partial[wave + i * nw] = ss;   // chunk (threadIdx.x + i * nthreads) / 64
   }
-  ss = wave_sum(ss);
-  if (lane == 0) partial[wave] = ss;
   __syncthreads();
   float tot = 0.0f;
-  const int nw = nthreads >> 6;
-  for (int i = 0; i < nw; ++i) tot = tot + partial[i];
+  for (int c = 0; c < nw * CPT; ++c) tot = tot + partial[c];
   const float inv = rsqrtf(tot * inv_hidden + eps);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -389,7 +394,11 @@ hipError_t launch_finalize_rmsnorm(const Routed& r, const uint16_t* residual,
                                    uint16_t* residual_out, uint16_t* normed,
                                    hipStream_t stream) {
   const GatherArgs a = make_args(r);
-  int threads = ((a.h8 + kWaveLanes - 1) / kWaveLanes) * kWaveLanes;
+  // One thread per 16-byte column vector (one wave per 512-column chunk) up
+  // to 16 waves; from kNormHalfWidthFrom tokens on, half as many waves with
+  // two vectors per thread when the chunk count is even.
+  int threads = a.nchunks * kWaveLanes;
+  if (a.tokens >= kNormHalfWidthFrom && a.nchunks % 2 == 0) threads /= 2;
   if (threads > kNormMaxThreads) threads = kNormMaxThreads;
   const int cpt = (a.h8 + threads - 1) / threads;   // 1 or 2 (hidden <= 16384)
   const float inv_hidden = 1.0f / (float)r.hidden;

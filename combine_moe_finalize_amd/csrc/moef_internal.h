@@ -63,6 +63,8 @@ constexpr int kVecElems = 8;                           // bf16 per 16-byte vecto
 constexpr int kChunkCols = kWaveLanes * kVecElems;     // columns per wave pass
 constexpr int kWavesPerBlock = 4;                      // plain / quant kernels
 constexpr int kNormMaxThreads = 1024;                  // RMSNorm: one block per token
+constexpr int kNormMaxChunks = MOEF_MAX_HIDDEN_RMSNORM / (kVecElems * kWaveLanes);
+constexpr int64_t kNormHalfWidthFrom = 1024;           // tokens: half-width RMSNorm blocks
 constexpr int64_t kActQuantPairFrom = int64_t(1) << 21;  // act quant: 2 vectors per lane
 constexpr int64_t kMaxUnits = (int64_t(1) << 31) - 1;  // (token, chunk) pairs
 

@@ -558,3 +558,33 @@ def test_non_finite_values():
     assert fin.tolist() == [False, False, False, True]
     g, o = F.bf16_to_f64(h_bits(nm)[fin]), F.bf16_to_f64(m_nm[fin])
     assert np.all(np.abs(g - o) <= ulp_bf16(o)), "normed of the finite token"
+
+
+def test_results_do_not_depend_on_batch_size():
+    """The same tokens give the same bits whether they come in a batch of
+    1100 tokens or of 40: the RMSNorm epilogue switches to half-width
+    workgroups from 1024 tokens on, and sums its per-chunk partials in the
+    same order either way. Plain and quant outputs are checked too."""
+    T, n = 1100, 40
+    wl = W.make_workload(T, 7168, 256, 8, rsf=2.5, seed=77, with_residual=True)
+    kw = device_inputs(wl)
+    res, gam = d_bf16(wl.residual), d_bf16(wl.gamma)
+    small = dict(kw, expanded_idx_to_permuted_idx=kw["expanded_idx_to_permuted_idx"][:n].contiguous(),
+                 topk_weights=kw["topk_weights"][:n].contiguous(),
+                 shared_out=kw["shared_out"][:n].contiguous())
+    announce(f"batch invariance T={T} vs {n}")
+    ro, nm = M.moe_finalize_residual_rmsnorm(**kw, residual=res, gamma=gam, eps=wl.eps)
+    ro_s, nm_s = M.moe_finalize_residual_rmsnorm(**small, residual=res[:n].contiguous(),
+                                                 gamma=gam, eps=wl.eps)
+    out, out_s = M.moe_finalize(**kw), M.moe_finalize(**small)
+    (q, s), (q_s, s_s) = M.moe_finalize_quant_ue8m0(**kw), M.moe_finalize_quant_ue8m0(**small)
+    torch.cuda.synchronize()
+    for big, sm, what in ((ro, ro_s, "residual_out"), (nm, nm_s, "normed"), (out, out_s, "out"),
+                          (q, q_s, "codes"), (s, s_s, "scales")):
+        assert torch.equal(big[:n].view(torch.uint8), sm.view(torch.uint8)), what
+    m_ro, m_nm, _ = O.finalize_residual_rmsnorm_mirror(
+        wl.gemm2_out, wl.idx, residual=wl.residual, gamma=wl.gamma, eps=wl.eps,
+        weights_f32=wl.weights, shared=wl.shared, rsf=wl.rsf)
+    assert_bits_equal(h_bits(ro), m_ro, "residual_out")
+    g, o = F.bf16_to_f64(h_bits(nm)), F.bf16_to_f64(m_nm)
+    assert np.all(np.abs(g - o) <= ulp_bf16(o)), "normed"
