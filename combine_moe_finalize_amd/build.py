@@ -97,7 +97,25 @@ def build_host_checks() -> str:
     return HOST_CHECKS
 
 
+HOST_STUB_LIB = os.path.join(os.path.dirname(C_DRIVER_SRC), "libmoef_host_stub.so")
+
+
+def build_host_stub_lib() -> str:
+    """The C-ABI entry points linked against the host-only launch stubs as a
+    shared library (no GPU code runs; the stubs count launches), for tests
+    that drive the argument checks from Python."""
+    cdir = os.path.dirname(C_DRIVER_SRC)
+    cmd = [hipcc(), "-O1", "-std=c++17", "-fPIC", "-shared", "-I", INCLUDE, "-I", CSRC,
+           os.path.join(CSRC, "moef_api.hip"), os.path.join(cdir, "launch_stub.cpp"),
+           "-o", HOST_STUB_LIB]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stderr}")
+    return HOST_STUB_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_c_driver())
     print(build_host_checks())
+    print(build_host_stub_lib())

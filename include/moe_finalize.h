@@ -111,7 +111,8 @@ enum moef_status {
  *              expert outputs. Only rows named by the index map are read, so
  *              padding may hold anything (NaN) and cost does not grow with
  *              num_rows. May be NULL only if num_rows == 0.
- *  num_rows    P >= 0, rows in gemm2_out.
+ *  num_rows    P >= 0, rows in gemm2_out; at most 2^31 - 1 (rows are named
+ *              by int32 indices), else MOEF_ERR_UNSUPPORTED.
  *  expanded_idx_to_permuted_idx  int32 [num_tokens, top_k]: the gemm2_out
  *              row of slot (t, k), at element t * top_k + k.
  *  topk_weights / topk_packed    routing weights, exactly one non-NULL.
@@ -119,6 +120,9 @@ enum moef_status {
  *  routed_scaling_factor         folded into every routed weight (1.0: none).
  *  out         bf16 [num_tokens, hidden], written.
  *  err_flag    optional device int32 (see conventions).
+ *  num_tokens, hidden, top_k  shape rules of the conventions, and
+ *              num_tokens * ceil(hidden / 512) <= 2^31 - 1 (one wave per
+ *              512-column chunk of a token), else MOEF_ERR_UNSUPPORTED.
  */
 int moe_finalize(const uint16_t* gemm2_out, int64_t num_rows,
                  const int32_t* expanded_idx_to_permuted_idx,
