@@ -202,6 +202,12 @@ int moe_finalize_quant_ue8m0(const uint16_t* gemm2_out, int64_t num_rows,
  *  out          bf16 [num_tokens, hidden] = bf16(+0 + p_0 + ... + p_{R-1}
  *               [+ shared]), fp32 adds in rank order, one rounding.
  *  hidden       a multiple of 8. num_tokens == 0 is a no-op.
+ *  Errors: num_tokens < 0, hidden < 1 or num_partials outside
+ *  [1, MOEF_MAX_EP_PARTIALS] give BAD_SHAPE; hidden not a multiple of 8 or
+ *  above MOEF_MAX_HIDDEN, or num_tokens * hidden / 8 above (2^31 - 1) * 256,
+ *  give UNSUPPORTED; a NULL partials or out gives NULL_POINTER; a pointer
+ *  that is not 16-byte aligned gives MISALIGNED; out overlapping the partials
+ *  or shared_out gives BAD_ALIAS.
  */
 int moe_finalize_ep_combine(const uint16_t* partials, int32_t num_partials,
                             const uint16_t* shared_out, uint16_t* out,
@@ -255,6 +261,10 @@ int moe_allreduce_residual_rmsnorm(const uint16_t* const* rank_outputs, int32_t 
  *  expert_ids  int32 [n] = (uint32)packed >> 16, or NULL to skip.
  *  weights     float32 [n] = the bf16 weight widened exactly, or NULL.
  *  At least one output must be non-NULL. n == 0 is a no-op.
+ *  Errors: n < 0 gives BAD_SHAPE; n above (2^31 - 1) * 256 gives UNSUPPORTED;
+ *  a NULL packed, or both outputs NULL, gives NULL_POINTER; a pointer that is
+ *  not 4-byte aligned gives MISALIGNED; an output that overlaps packed or the
+ *  other output gives BAD_ALIAS.
  */
 int moe_topk_packed_decode(const int32_t* packed, int64_t n,
                            int32_t* expert_ids, float* weights, void* stream);
@@ -278,6 +288,11 @@ int moe_topk_packed_decode(const int32_t* packed, int64_t n,
  *  topk_packed    int32 [num_tokens, top_k] or NULL: (id << 16) | bf16 bits of
  *                 the weight, rounded to nearest even.
  *  num_tokens == 0 is a no-op.
+ *  Errors: num_tokens < 0, num_experts < 1 or top_k outside [1, min(E, 16)]
+ *  give BAD_SHAPE; num_experts above MOEF_MAX_GATE_EXPERTS or num_tokens
+ *  above 2^31 - 5 give UNSUPPORTED; a NULL router_logits or topk_ids gives
+ *  NULL_POINTER; a pointer that is not 4-byte aligned gives MISALIGNED; an
+ *  output that overlaps the logits or another output gives BAD_ALIAS.
  */
 int moe_topk_sigmoid_gate(const float* router_logits, int64_t num_tokens,
                           int32_t num_experts, int32_t top_k,
@@ -303,6 +318,13 @@ int moe_topk_sigmoid_gate(const float* router_logits, int64_t num_tokens,
  *              (correctly rounded fp32; 1 for an all-zero block),
  *              codes = e4m3(fp32(x / scale)), nearest even.
  *  num_tokens == 0 is a no-op.
+ *  Errors: num_tokens < 0 or hidden < 1 give BAD_SHAPE; hidden not a
+ *  multiple of 128 or above MOEF_MAX_HIDDEN, num_tokens above 2^31 - 1, or
+ *  num_tokens * ceil(hidden / 512) above 2^31 - 1 give UNSUPPORTED; a NULL x,
+ *  out_e4m3 or scale gives NULL_POINTER (a NULL scale is reported before the
+ *  shape checks when num_tokens > 0); x not 16-, out_e4m3 not 8- or
+ *  scale_f32 not 4-byte aligned gives MISALIGNED; an output that overlaps x
+ *  or the other output gives BAD_ALIAS.
  */
 int moe_act_quant_fp8_ue8m0(const uint16_t* x, int64_t num_tokens, int64_t hidden,
                             uint8_t* out_e4m3, uint8_t* scale_e8m0, void* stream);
