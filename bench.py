@@ -13,6 +13,8 @@ UE8M0 / E4M3 quantization.
 Printed: one JSON line with
   value      algorithmic GB/s of the whole step (bytes the method must move /
              wall time per step, inputs resident),
+  ceilings   a same-session device-copy rate and the headline kernel's rate as
+             a fraction of it (the kernel moves 95% reads, a copy half),
   roofline   the kernel's algorithmic bytes per launch / its average duration
              (HIP events recorded on the launch stream around the K timed
              launches, divided by K), against the 8 TB/s HBM peak;
@@ -345,6 +347,27 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
     return rows
 
 
+def copy_ceiling(torch, nbytes=1 << 30, reps=20):
+    """Same-session device-copy rate in GB/s: torch's device-to-device copy of
+    nbytes (2 x nbytes moved per copy), median of `reps` event-timed copies."""
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda:0").fill_(3)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / float(np.median(times)) / 1e9
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -443,6 +466,13 @@ def main():
                                          f"timed launches, divided by {args.steps}",
                      "algorithmic_bytes_per_launch": nbytes},
     }
+    copy_gbs = copy_ceiling(torch)
+    log(f"same-session device copy: {copy_gbs:.0f} GB/s")
+    result["ceilings"] = {
+        "device_copy_gbs": round(copy_gbs, 1),
+        "device_copy_method": "torch device-to-device copy of 1 GiB (2 GiB moved), median of "
+                              "20 event-timed copies, after the timed launches",
+        "headline_frac_of_copy": round(achieved / copy_gbs, 4)}
     # us/call of the same operation on the first T tokens of the same workload,
     # T = 1, 2, 4, ..., 8192, per call under HIP-graph replay
     curve = {}
