@@ -13,8 +13,10 @@ UE8M0 / E4M3 quantization.
 Printed: one JSON line with
   value      algorithmic GB/s of the whole step (bytes the method must move /
              wall time per step, inputs resident),
-  ceilings   a same-session device-copy rate and the headline kernel's rate as
-             a fraction of it (the kernel moves 95% reads, a copy half),
+  ceilings   same-session streaming read and copy rates (the bandwidth probe
+             kernels) and torch's device copy, with the headline kernel's rate
+             as a fraction of the read and copy rates (the kernel moves 95%
+             reads, a copy half),
   roofline   the kernel's algorithmic bytes per launch / its average duration
              (HIP events recorded on the launch stream around the K timed
              launches, divided by K), against the 8 TB/s HBM peak;
@@ -347,15 +349,46 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
     return rows
 
 
-def copy_ceiling(torch, nbytes=1 << 30, reps=20):
-    """Same-session device-copy rate in GB/s: torch's device-to-device copy of
-    nbytes (2 x nbytes moved per copy), median of `reps` event-timed copies."""
-    src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda:0").fill_(3)
+def ceilings(torch, nbytes=1 << 30):
+    """Same-session HBM rates in GB/s: the streaming read and copy probes
+    (moe_bandwidth_probes.h) over `nbytes`, 10 back-to-back launches between
+    two events, median of 5; and torch's own device-to-device copy, median
+    of 20 event-timed copies. A copy moves 2 x nbytes."""
+    import ctypes
+    from combine_moe_finalize_amd._paths import PROBE_LIB_PATH
+    P = ctypes.CDLL(PROBE_LIB_PATH)                  # fails loudly when it is not built
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    P.moef_probe_read.argtypes = [vp, i64, vp, vp]
+    P.moef_probe_copy.argtypes = [vp, vp, i64, vp]
+    src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def per_launch_s(fn, n=10, reps=5):
+        for _ in range(2):
+            assert fn() == 0
+        times = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3 / n)
+        return float(np.median(times))
+
+    read = nbytes / per_launch_s(lambda: P.moef_probe_read(src.data_ptr(), nbytes,
+                                                           sink.data_ptr(), stream)) / 1e9
+    copy = 2 * nbytes / per_launch_s(lambda: P.moef_probe_copy(src.data_ptr(), dst.data_ptr(),
+                                                               nbytes, stream)) / 1e9
+    torch.cuda.synchronize()
+    if int(sink.item()) != 0 or not torch.equal(dst[:1 << 20], src[:1 << 20]):
+        raise RuntimeError("bandwidth probes: unexpected output")
     times = []
-    for _ in range(reps):
+    for _ in range(20):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -363,9 +396,10 @@ def copy_ceiling(torch, nbytes=1 << 30, reps=20):
         b.record()
         torch.cuda.synchronize()
         times.append(a.elapsed_time(b) * 1e-3)
-    del src, dst
+    torch_copy = 2 * nbytes / float(np.median(times)) / 1e9
+    del src, dst, sink
     torch.cuda.empty_cache()
-    return 2 * nbytes / float(np.median(times)) / 1e9
+    return read, copy, torch_copy
 
 
 # ------------------------------------------------------------------ main
@@ -466,12 +500,16 @@ def main():
                                          f"timed launches, divided by {args.steps}",
                      "algorithmic_bytes_per_launch": nbytes},
     }
-    copy_gbs = copy_ceiling(torch)
-    log(f"same-session device copy: {copy_gbs:.0f} GB/s")
+    read_gbs, copy_gbs, torch_copy_gbs = ceilings(torch)
+    log(f"same-session ceilings: read {read_gbs:.0f}, copy {copy_gbs:.0f}, torch copy "
+        f"{torch_copy_gbs:.0f} GB/s")
     result["ceilings"] = {
-        "device_copy_gbs": round(copy_gbs, 1),
-        "device_copy_method": "torch device-to-device copy of 1 GiB (2 GiB moved), median of "
-                              "20 event-timed copies, after the timed launches",
+        "read_gbs": round(read_gbs, 1), "copy_gbs": round(copy_gbs, 1),
+        "torch_copy_gbs": round(torch_copy_gbs, 1),
+        "method": "1 GiB streams after the timed launches: the read and copy probes "
+                  "(moe_bandwidth_probes.h), 10 launches per event pair, median of 5; "
+                  "torch's device copy, median of 20",
+        "headline_frac_of_read": round(achieved / read_gbs, 4),
         "headline_frac_of_copy": round(achieved / copy_gbs, 4)}
     # us/call of the same operation on the first T tokens of the same workload,
     # T = 1, 2, 4, ..., 8192, per call under HIP-graph replay

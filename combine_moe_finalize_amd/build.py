@@ -14,10 +14,10 @@ import subprocess
 import sys
 
 try:
-    from ._paths import CSRC, INCLUDE, LIB_DIR, LIB_PATH
+    from ._paths import CSRC, INCLUDE, LIB_DIR, LIB_PATH, PROBE_LIB_PATH
 except ImportError:            # run as a script
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-    from _paths import CSRC, INCLUDE, LIB_DIR, LIB_PATH
+    from _paths import CSRC, INCLUDE, LIB_DIR, LIB_PATH, PROBE_LIB_PATH
 
 SOURCES = ["moef_api.hip", "finalize_kernels.hip", "routing_kernels.hip", "act_quant_kernels.hip",
            "allreduce_kernels.hip"]
@@ -55,6 +55,21 @@ def build(verbose: bool = False) -> str:
         print(msgs, file=sys.stderr)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+def build_probes() -> str:
+    """Compile the streaming read / copy probe library the benchmark measures
+    its same-session ceilings with (always, like the main library)."""
+    os.makedirs(LIB_DIR, exist_ok=True)
+    tmp = PROBE_LIB_PATH + ".tmp"
+    cmd = [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall",
+           "-I", INCLUDE, os.path.join(CSRC, "bandwidth_probes.hip"), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB_PATH)
+    return PROBE_LIB_PATH
 
 
 C_DRIVER_SRC = os.path.join(os.path.dirname(os.path.dirname(LIB_DIR)), "tests", "c",
@@ -116,6 +131,7 @@ def build_host_stub_lib() -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probes())
     print(build_c_driver())
     print(build_host_checks())
     print(build_host_stub_lib())

@@ -1,0 +1,45 @@
+/*
+ * moe_bandwidth_probes.h - streaming read and copy kernels that measure the
+ * HBM rates one MI355X reaches in the same session as a benchmark, so the
+ * finalize kernels can be reported against a measured ceiling beside the
+ * 8 TB/s specification. Measurement infrastructure: the finalize library does
+ * not use them.
+ *
+ * Both kernels read `bytes` from `src` as 16-byte vectors with non-temporal
+ * loads, each lane keeping four loads in flight; one workgroup covers 16 KiB.
+ *
+ *  src, dst  device pointers, 16-byte aligned, `bytes` long each.
+ *  bytes     a positive multiple of MOEF_PROBE_GRAIN.
+ *  sink      device uint32 (read probe): written only when the XOR of a
+ *            lane's 64 bytes equals 0x9E3779B9, which keeps the loads from
+ *            being optimized away; with all-zero input it is never written.
+ *  stream    hipStream_t as void* (NULL: the null stream); the call returns
+ *            without waiting.
+ *
+ * Return value: 0, or 1 (a NULL pointer), 2 (bytes not a positive multiple
+ * of MOEF_PROBE_GRAIN, or more than 2^31 - 1 grains), 4 (src or dst not
+ * 16-byte aligned, sink not 4-byte aligned), 6 (dst overlaps src), 7 (the
+ * HIP runtime rejected the launch). Checks run before any HIP call.
+ */
+#ifndef MOE_BANDWIDTH_PROBES_H
+#define MOE_BANDWIDTH_PROBES_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOEF_PROBE_GRAIN 16384
+
+/* Reads every byte of src once. */
+int moef_probe_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
+/* dst = src, byte for byte, with non-temporal loads and stores. */
+int moef_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_BANDWIDTH_PROBES_H */
