@@ -81,24 +81,32 @@ def describe(wl, packed, oob):
             f"shared={wl.shared is not None} oob={oob}")
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(64))
 def test_random_finalize(case):
-    rng = np.random.default_rng(1000 + case)
+    check_finalize(1000 + case)
+
+
+def check_finalize(seed):
+    rng = np.random.default_rng(seed)
     wl, idx, packed, oob = draw(rng, "plain")
-    announce(f"random finalize #{case}: {describe(wl, packed, oob)}")
+    announce(f"random finalize seed {seed}: {describe(wl, packed, oob)}")
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     out = M.moe_finalize(**device_args(wl, idx, packed), err_flag=err)
     torch.cuda.synchronize()
     ref, flag = O.finalize_mirror(wl.gemm2_out, idx, **oracle_args(wl, idx, packed))
-    assert_bits_equal(h_bits(out), ref, f"case {case}")
+    assert_bits_equal(h_bits(out), ref, f"seed {seed}")
     assert int(err.item()) == flag == (1 if oob else 0)
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(48))
 def test_random_residual_rmsnorm(case):
-    rng = np.random.default_rng(2000 + case)
+    check_residual_rmsnorm(2000 + case)
+
+
+def check_residual_rmsnorm(seed):
+    rng = np.random.default_rng(seed)
     wl, idx, packed, oob = draw(rng, "rmsnorm")
-    announce(f"random residual+rmsnorm #{case}: {describe(wl, packed, oob)}")
+    announce(f"random residual+rmsnorm seed {seed}: {describe(wl, packed, oob)}")
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     ro, nm = M.moe_finalize_residual_rmsnorm(**device_args(wl, idx, packed),
                                              residual=d_bf16(wl.residual), gamma=d_bf16(wl.gamma),
@@ -107,29 +115,37 @@ def test_random_residual_rmsnorm(case):
     m_ro, m_nm, flag = O.finalize_residual_rmsnorm_mirror(
         wl.gemm2_out, idx, residual=wl.residual, gamma=wl.gamma, eps=wl.eps,
         **oracle_args(wl, idx, packed))
-    assert_bits_equal(h_bits(ro), m_ro, f"case {case} residual_out")
+    assert_bits_equal(h_bits(ro), m_ro, f"seed {seed} residual_out")
     g, o = F.bf16_to_f64(h_bits(nm)), F.bf16_to_f64(m_nm)
-    assert np.all(np.abs(g - o) <= ulp_bf16(o)), f"case {case} normed"
+    assert np.all(np.abs(g - o) <= ulp_bf16(o)), f"seed {seed} normed"
     assert int(err.item()) == flag == (1 if oob else 0)
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(48))
 def test_random_quant(case):
-    rng = np.random.default_rng(3000 + case)
+    check_quant(3000 + case)
+
+
+def check_quant(seed):
+    rng = np.random.default_rng(seed)
     wl, idx, packed, oob = draw(rng, "quant")
-    announce(f"random quant #{case}: {describe(wl, packed, oob)}")
+    announce(f"random quant seed {seed}: {describe(wl, packed, oob)}")
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     q, s = M.moe_finalize_quant_ue8m0(**device_args(wl, idx, packed), err_flag=err)
     torch.cuda.synchronize()
     mq, ms, flag = O.finalize_quant_mirror(wl.gemm2_out, idx, **oracle_args(wl, idx, packed))
-    assert_bits_equal(s.cpu().numpy(), ms, f"case {case} scales")
-    assert_bits_equal(q.cpu().numpy(), mq, f"case {case} codes")
+    assert_bits_equal(s.cpu().numpy(), ms, f"seed {seed} scales")
+    assert_bits_equal(q.cpu().numpy(), mq, f"seed {seed} codes")
     assert int(err.item()) == flag == (1 if oob else 0)
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(48))
 def test_random_gate(case):
-    rng = np.random.default_rng(4000 + case)
+    check_gate(4000 + case)
+
+
+def check_gate(seed):
+    rng = np.random.default_rng(seed)
     E = int(rng.integers(1, 513))
     k = int(rng.integers(1, min(E, 16) + 1))
     T = int(rng.integers(1, 400))
@@ -137,12 +153,12 @@ def test_random_gate(case):
         lg = rng.integers(-4, 5, size=(T, E)).astype(np.float32)        # many exact ties
         lg[rng.random((T, E)) < 0.02] = np.nan
     else:
-        lg = W.router_logits(T, E, seed=case, scale=float(rng.uniform(0.5, 4.0)))
-    announce(f"random gate #{case}: T={T} E={E} k={k}")
+        lg = W.router_logits(T, E, seed=seed, scale=float(rng.uniform(0.5, 4.0)))
+    announce(f"random gate seed {seed}: T={T} E={E} k={k}")
     ids, w, pk = M.moe_topk_sigmoid_gate(torch.from_numpy(lg).to(DEV), k)
     torch.cuda.synchronize()
     oid, ow, _ = RT.topk_sigmoid_gate(lg, k)
-    assert np.array_equal(ids.cpu().numpy(), oid), f"case {case} ids"
+    assert np.array_equal(ids.cpu().numpy(), oid), f"seed {seed} ids"
     w = w.cpu().numpy()
     fin = np.isfinite(ow)
     assert np.all(np.abs(w[fin] - ow[fin]) <= 32 * 2.0 ** -24 * np.abs(ow[fin]) + 1e-38)
@@ -150,29 +166,37 @@ def test_random_gate(case):
     assert np.array_equal(pk.cpu().numpy().view(np.uint32) >> 16, oid.astype(np.uint32))
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(24))
 def test_random_act_quant(case):
-    rng = np.random.default_rng(5000 + case)
+    check_act_quant(5000 + case)
+
+
+def check_act_quant(seed):
+    rng = np.random.default_rng(seed)
     H = 128 * int(rng.integers(1, 129))
     T = int(rng.integers(1, max(2, MAX_ELEMS // H)))
-    x = W.activations(T, H, seed=case)
-    announce(f"random act quant #{case}: T={T} H={H}")
+    x = W.activations(T, H, seed=seed)
+    announce(f"random act quant seed {seed}: T={T} H={H}")
     xd = d_bf16(x)
     q1, s1 = M.moe_act_quant_fp8_ue8m0(xd)
     q2, s2 = M.moe_act_quant_fp8_amax(xd)
     torch.cuda.synchronize()
     oq1, os1 = A.act_quant_ue8m0(x)
     oq2, os2 = A.act_quant_amax(x)
-    assert_bits_equal(s1.cpu().numpy(), os1, f"case {case} ue8m0 scales")
-    assert_bits_equal(q1.cpu().numpy(), oq1, f"case {case} ue8m0 codes")
+    assert_bits_equal(s1.cpu().numpy(), os1, f"seed {seed} ue8m0 scales")
+    assert_bits_equal(q1.cpu().numpy(), oq1, f"seed {seed} ue8m0 codes")
     assert_bits_equal(s2.cpu().numpy().view(np.uint32), os2.view(np.uint32),
-                      f"case {case} amax scales")
-    assert_bits_equal(q2.cpu().numpy(), oq2, f"case {case} amax codes")
+                      f"seed {seed} amax scales")
+    assert_bits_equal(q2.cpu().numpy(), oq2, f"seed {seed} amax codes")
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(24))
 def test_random_combine_and_allreduce(case):
-    rng = np.random.default_rng(6000 + case)
+    check_combine_and_allreduce(6000 + case)
+
+
+def check_combine_and_allreduce(seed):
+    rng = np.random.default_rng(seed)
     R = int(rng.integers(1, 17))
     H = 8 * int(rng.integers(1, 2049))
     T = int(rng.integers(1, max(2, MAX_ELEMS // (H * R) + 1)))
@@ -181,13 +205,13 @@ def test_random_combine_and_allreduce(case):
     sh = W.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     res = W.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     gam = W.to_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32))
-    announce(f"random combine/all-reduce #{case}: R={R} T={T} H={H}")
+    announce(f"random combine/all-reduce seed {seed}: R={R} T={T} H={H}")
     eo = M.moe_finalize_ep_combine(d_bf16(parts), shared_out=d_bf16(sh))
     ro, nm = M.moe_allreduce_residual_rmsnorm([d_bf16(p) for p in parts], residual=d_bf16(res),
                                               gamma=d_bf16(gam))
     torch.cuda.synchronize()
-    assert_bits_equal(h_bits(eo), O.ep_combine_mirror(parts, sh), f"case {case} combine")
+    assert_bits_equal(h_bits(eo), O.ep_combine_mirror(parts, sh), f"seed {seed} combine")
     m_ro, m_nm = O.allreduce_residual_rmsnorm_mirror(parts, res, gam)
-    assert_bits_equal(h_bits(ro), m_ro, f"case {case} residual_out")
+    assert_bits_equal(h_bits(ro), m_ro, f"seed {seed} residual_out")
     g, o = F.bf16_to_f64(h_bits(nm)), F.bf16_to_f64(m_nm)
-    assert np.all(np.abs(g - o) <= ulp_bf16(o)), f"case {case} normed"
+    assert np.all(np.abs(g - o) <= ulp_bf16(o)), f"seed {seed} normed"
