@@ -39,16 +39,13 @@ __global__ void __launch_bounds__(kNormMaxThreads)
 allreduce_rmsnorm_kernel(RankPtrs ranks, int R, int h8, const u32x4* residual,
                          const u32x4* __restrict__ gamma, float eps, float inv_hidden,
                          u32x4* residual_out, u32x4* __restrict__ normed) {
-  __shared__ float partial[kNormMaxThreads / kWaveLanes];
+  __shared__ float partial[kNormMaxChunks];
   const int t = blockIdx.x;
   const int nthreads = blockDim.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)t * h8;
 
   float ro[CPT][8];
   u32x4 gv[CPT];
-  float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int colv = threadIdx.x + i * nthreads;
@@ -78,31 +75,16 @@ allreduce_rmsnorm_kernel(RankPtrs ranks, int R, int h8, const u32x4* residual,
     for (int e = 0; e < 8; ++e) acc[e] = acc[e] + x[e];
     const u32x4 rb = pack8_rne(acc);
     unpack8(rb, ro[i]);                               // the stored bf16 residual_out
+    float ss = 0.0f;
     if (active) {
       __builtin_nontemporal_store(rb, residual_out + row + colv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = ss + ro[i][e] * ro[i][e];
     }
+    put_chunk_sum(ss, i, partial);
   }
-  ss = wave_sum(ss);
-  if (lane == 0) partial[wave] = ss;
-  __syncthreads();
-  float tot = 0.0f;
-  const int nw = nthreads >> 6;
-  for (int i = 0; i < nw; ++i) tot = tot + partial[i];
-  const float inv = rsqrtf(tot * inv_hidden + eps);
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int colv = threadIdx.x + i * nthreads;
-    if (colv < h8) {
-      float g[8];
-      unpack8(gv[i], g);
-      float n[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) n[e] = (ro[i][e] * inv) * g[e];
-      __builtin_nontemporal_store(pack8_rne(n), normed + row + colv);
-    }
-  }
+  const float inv = row_inv_rms<CPT>(partial, inv_hidden, eps);
+  store_normed<CPT>(ro, gv, inv, h8, normed + row);
 }
 
 template <int V>

@@ -1,6 +1,7 @@
 // Device helpers shared by the gfx950 kernels of this library: bf16 and
 // FP8 E4M3 conversions (gfx950 hardware converters), 16-byte vector packing,
-// wavefront reductions and the 1 x 128 block power-of-two (UE8M0) scale rule.
+// wavefront reductions, the RMSNorm of a row held by one workgroup, and the
+// 1 x 128 block power-of-two (UE8M0) scale rule.
 // Internal; included by the kernel translation units only.
 #pragma once
 
@@ -49,6 +50,51 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// ---------------------------------------------------- RMSNorm of one row
+// One workgroup holds one row; lane t of it owns the 16-byte column vectors
+// t + i * blockDim.x, i < CPT, so wave w's vector i is 512-column chunk
+// w + i * (blockDim.x / 64).
+
+// Records the sum of squares of vector i of every lane of this wave (one
+// 512-column chunk) in partial[chunk]. Called once per vector, as soon as
+// that vector's sum is known.
+__device__ __forceinline__ void put_chunk_sum(float ss, int i, float* partial) {
+  const float v = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) partial[(threadIdx.x >> 6) + i * (blockDim.x >> 6)] = v;
+}
+
+// 1 / sqrt(sum / hidden + eps) of the row, from the chunk sums put_chunk_sum
+// recorded, added in chunk order, so the value does not depend on how many
+// waves share the row. Every lane gets the same value. Contains the
+// workgroup barrier that makes the chunk sums visible.
+template <int CPT>
+__device__ __forceinline__ float row_inv_rms(const float* partial, float inv_hidden, float eps) {
+  __syncthreads();
+  const int nchunks = (blockDim.x >> 6) * CPT;
+  float tot = 0.0f;
+  for (int c = 0; c < nchunks; ++c) tot = tot + partial[c];
+  return rsqrtf(tot * inv_hidden + eps);
+}
+
+// normed = bf16((x * inv) * gamma) for the lane's CPT vectors of the row,
+// x being the stored bf16 values (fp32 math); vectors past h8 are skipped.
+template <int CPT>
+__device__ __forceinline__ void store_normed(const float x[CPT][8], const u32x4 gv[CPT],
+                                             float inv, int h8, u32x4* __restrict__ normed_row) {
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int colv = threadIdx.x + i * blockDim.x;
+    if (colv < h8) {
+      float g[8];
+      unpack8(gv[i], g);
+      float n[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) n[e] = (x[i][e] * inv) * g[e];
+      __builtin_nontemporal_store(pack8_rne(n), normed_row + colv);
+    }
+  }
 }
 
 // ------------------------------------------- 1 x 128 block quantization

@@ -51,7 +51,7 @@ using namespace dev;
 // Kernel-side view of one routed call.
 struct GatherArgs {
   const u32x4* g2;        // gemm2_out as 16-byte vectors, row stride h8
-  int64_t num_rows;
+  int32_t num_rows;       // <= 2^31 - 1: rows are named by int32 indices
   const int32_t* idx;     // [T, k]
   const uint32_t* w;      // [T, k] fp32 bits or packed words
   const u32x4* shared;    // [T, h8] or nullptr
@@ -88,7 +88,7 @@ __device__ __forceinline__ void load_route(const GatherArgs& a, int t,
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     w[j] = __uint_as_float(a.packed ? (word[j] << 16) : word[j]) * a.rsf;
-    if ((int64_t)row[j] >= a.num_rows) {   // out of range: skip and report
+    if (row[j] >= a.num_rows) {            // out of range: skip and report
       oob = true;
       row[j] = -1;
     }                                      // negative: expert not local, skip
@@ -183,14 +183,9 @@ __global__ void __launch_bounds__(kNormMaxThreads)
 finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __restrict__ gamma,
                         float eps, float inv_hidden, u32x4* residual_out,
                         u32x4* __restrict__ normed) {
-  // One partial sum of squares per 512-column chunk, summed in chunk order:
-  // the result does not depend on how many waves share the row.
   __shared__ float partial[kNormMaxChunks];
   const int t = blockIdx.x;
   const int nthreads = blockDim.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nw = nthreads >> 6;
 
   const u32x4* res_row = residual + (int64_t)t * a.h8;
   // row-independent operands first: shared, residual and gamma vectors
@@ -223,25 +218,10 @@ finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __rest
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = ss + ro[i][e] * ro[i][e];
     }
-    ss = wave_sum(ss);
-    if (lane == 0) partial[wave + i * nw] = ss;   // chunk (threadIdx.x + i * nthreads) / 64
+    put_chunk_sum(ss, i, partial);
   }
-  __syncthreads();
-  float tot = 0.0f;
-  for (int c = 0; c < nw * CPT; ++c) tot = tot + partial[c];
-  const float inv = rsqrtf(tot * inv_hidden + eps);
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int colv = threadIdx.x + i * nthreads;
-    if (colv < a.h8) {
-      float g[8];
-      unpack8(gv[i], g);
-      float n[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) n[e] = (ro[i][e] * inv) * g[e];
-      __builtin_nontemporal_store(pack8_rne(n), normed + (int64_t)t * a.h8 + colv);
-    }
-  }
+  const float inv = row_inv_rms<CPT>(partial, inv_hidden, eps);
+  store_normed<CPT>(ro, gv, inv, a.h8, normed + (int64_t)t * a.h8);
 }
 
 // ------------------------------------------------------- UE8M0 / E4M3 quant
@@ -356,7 +336,7 @@ hipError_t dispatch_top_k(int k, F&& f) {
 GatherArgs make_args(const Routed& r) {
   GatherArgs a;
   a.g2 = reinterpret_cast<const u32x4*>(r.gemm2_out);
-  a.num_rows = r.num_rows;
+  a.num_rows = (int32_t)r.num_rows;       // validated <= INT32_MAX
   a.idx = r.idx;
   a.w = r.weights;
   a.shared = reinterpret_cast<const u32x4*>(r.shared);
