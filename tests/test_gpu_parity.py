@@ -588,3 +588,33 @@ def test_results_do_not_depend_on_batch_size():
     assert_bits_equal(h_bits(ro), m_ro, "residual_out")
     g, o = F.bf16_to_f64(h_bits(nm)), F.bf16_to_f64(m_nm)
     assert np.all(np.abs(g - o) <= ulp_bf16(o)), "normed"
+
+
+@pytest.mark.parametrize("H", [1000, 4104, 5000, 16384])
+def test_rmsnorm_half_width_ragged(H):
+    """From 1024 tokens on, a row with an even number of 512-column chunks
+    takes half-width workgroups with two vectors per lane. Ragged hidden sizes
+    there: H=1000 (2 chunks, the second vector of most lanes past the row
+    end), 4104 (9 chunks: odd, stays full width), 5000 (10 chunks, partly
+    filled), 16384 (32 chunks, the widest workgroup either way). residual_out
+    is bit-exact to the mirror, normed within one ulp of the fp64 RMSNorm, and
+    the first tokens match a 16-token call bit for bit."""
+    T, k = 1024, 4
+    wl = W.make_workload(T, H, 32, k, rsf=2.5, seed=H, with_residual=True, log2_mag=(-4.0, 4.0))
+    kw = device_inputs(wl)
+    res, gam = d_bf16(wl.residual), d_bf16(wl.gamma)
+    announce(f"half-width rmsnorm T={T} H={H}")
+    ro, nm = M.moe_finalize_residual_rmsnorm(**kw, residual=res, gamma=gam, eps=wl.eps)
+    n = 16
+    small = dict(kw, expanded_idx_to_permuted_idx=kw["expanded_idx_to_permuted_idx"][:n],
+                 topk_weights=kw["topk_weights"][:n], shared_out=kw["shared_out"][:n])
+    ro_s, nm_s = M.moe_finalize_residual_rmsnorm(**small, residual=res[:n], gamma=gam, eps=wl.eps)
+    torch.cuda.synchronize()
+    m_ro, m_nm, _ = O.finalize_residual_rmsnorm_mirror(
+        wl.gemm2_out, wl.idx, residual=wl.residual, gamma=wl.gamma, eps=wl.eps,
+        weights_f32=wl.weights, shared=wl.shared, rsf=wl.rsf)
+    assert_bits_equal(h_bits(ro), m_ro, f"H={H} residual_out")
+    g, o = F.bf16_to_f64(h_bits(nm)), F.bf16_to_f64(m_nm)
+    assert np.all(np.abs(g - o) <= ulp_bf16(o)), f"H={H} normed"
+    assert torch.equal(ro[:n].view(torch.int16), ro_s.view(torch.int16))
+    assert torch.equal(nm[:n].view(torch.int16), nm_s.view(torch.int16))
