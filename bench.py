@@ -184,17 +184,37 @@ def e4m3_steps(a, b):
     return np.abs(line(a) - line(b))
 
 
-def cpu_baseline(wl, q_gpu=None, s_gpu=None, min_s=10.0, max_s=30.0, chunk=256,
-                 mirror_tokens=512):
-    """The oracle (fp64 truth finalize + UE8M0 quant), single thread, in
-    token chunks over the same workload, repeating passes until at least
-    min_s seconds of CPU work (stopping early at max_s).
+def host_threads():
+    """Host CPUs this process may run on, at most 16 (one GPU's share of a box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
 
-    With the GPU's codes and scale bytes given, the first pass's oracle
-    outputs are also compared with them after the timing: against the fp64
-    truth over every token (scale bytes equal, codes within one step), and
-    against the oracle's fp32 mirror of the kernels' operation order, untimed,
-    on the first mirror_tokens tokens (bit-exact)."""
+
+def oracle_chunk(O, wl, sl):
+    return O.finalize_quant_truth(wl.gemm2_out, wl.idx[sl], weights_f32=wl.weights[sl],
+                                  shared=wl.shared[sl], rsf=wl.rsf)
+
+
+def cpu_baseline(wl, q_gpu=None, s_gpu=None, min_s=10.0, max_s=30.0, chunk=256,
+                 mirror_tokens=512, threads=None, min_s_threads=5.0):
+    """The oracle (fp64 truth finalize + UE8M0 quant), as it stands, in token
+    chunks over the same workload.
+
+    One thread first, repeating passes until at least min_s seconds of CPU
+    work (stopping early at max_s); then, with threads > 1 (default: the
+    host CPUs available, at most 16), the same chunks spread over a thread
+    pool for at least min_s_threads seconds. The reported value is the
+    thread-pool rate (cores = its thread count), the one-thread rate beside it.
+
+    With the GPU's codes and scale bytes given, the first one-thread pass's
+    oracle outputs are also compared with them after the timing: against the
+    fp64 truth over every token (scale bytes equal, codes within one step),
+    and against the oracle's fp32 mirror of the kernels' operation order,
+    untimed, on the first mirror_tokens tokens (bit-exact)."""
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import finalize as O
     keep = q_gpu is not None
     t_codes = np.empty((wl.T, wl.H), np.uint8) if keep else None
@@ -204,8 +224,7 @@ def cpu_baseline(wl, q_gpu=None, s_gpu=None, min_s=10.0, max_s=30.0, chunk=256,
     while True:
         start = done % wl.T
         sl = slice(start, min(wl.T, start + chunk))
-        qc, sc, _ = O.finalize_quant_truth(wl.gemm2_out, wl.idx[sl], weights_f32=wl.weights[sl],
-                                           shared=wl.shared[sl], rsf=wl.rsf)
+        qc, sc, _ = oracle_chunk(O, wl, sl)
         if keep and done < wl.T:
             t_codes[sl], t_scales[sl] = qc, sc
         done += sl.stop - sl.start
@@ -213,11 +232,33 @@ def cpu_baseline(wl, q_gpu=None, s_gpu=None, min_s=10.0, max_s=30.0, chunk=256,
         if (el >= min_s and done % wl.T == 0) or el >= max_s:
             break
     dt = time.perf_counter() - t0
-    gbs = bytes_quant(done, wl.H, wl.top_k) / dt / 1e9
-    base = {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} tokens ({done / wl.T:.2f} passes over the T={wl.T} workload) "
-                      f"through the fp64 finalize + UE8M0/E4M3 quant oracle, numpy, one "
-                      f"thread, {dt:.1f} s"}
+    gbs1 = bytes_quant(done, wl.H, wl.top_k) / dt / 1e9
+    one = {"value": round(gbs1, 4), "cores": 1,
+           "sample": f"{done} tokens ({done / wl.T:.2f} passes over the T={wl.T} workload), "
+                     f"{dt:.1f} s"}
+    n_thr = host_threads() if threads is None else threads
+    base = {"value": round(gbs1, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{one['sample']} through the fp64 finalize + UE8M0/E4M3 quant oracle, "
+                      f"numpy, one thread"}
+    if n_thr > 1:
+        slices = [slice(a, min(wl.T, a + chunk)) for a in range(0, wl.T, chunk)]
+        mt_done, passes = 0, 0
+        t1 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=n_thr) as pool:
+            while True:
+                for _ in pool.map(lambda sl: oracle_chunk(O, wl, sl), slices):
+                    pass
+                mt_done += wl.T
+                passes += 1
+                if time.perf_counter() - t1 >= min_s_threads:
+                    break
+        dt_mt = time.perf_counter() - t1
+        base = {"value": round(bytes_quant(mt_done, wl.H, wl.top_k) / dt_mt / 1e9, 4),
+                "unit": "GB/s", "cores": n_thr, "kind": "oracle",
+                "sample": f"{mt_done} tokens ({passes} passes over the T={wl.T} workload) "
+                          f"through the fp64 finalize + UE8M0/E4M3 quant oracle, numpy, "
+                          f"{n_thr} threads over {chunk}-token chunks, {dt_mt:.1f} s",
+                "single_thread": one}
     if not keep:
         return base, None
     n = min(done, wl.T)

@@ -100,14 +100,16 @@ def test_parity_statistics_of_the_cpu_leg():
     wl = W.make_workload(40, 1024, 16, 8, rsf=2.5, seed=3, log2_mag=(-8.0, 8.0))
     q, s, _ = O.finalize_quant_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
                                       shared=wl.shared, rsf=wl.rsf)
-    base, par = bench.cpu_baseline(wl, q, s, min_s=0.0, max_s=60.0, chunk=16, mirror_tokens=24)
+    base, par = bench.cpu_baseline(wl, q, s, min_s=0.0, max_s=60.0, chunk=16, mirror_tokens=24,
+                                   threads=1)
     assert base["kind"] == "oracle" and base["cores"] == 1
     assert par["tokens_vs_fp64_truth"] == 40 and par["tokens_vs_fp32_mirror"] == 24
     assert par["code_mismatches_vs_mirror"] == 0 and par["scale_mismatches_vs_mirror"] == 0
     assert par["max_code_steps_vs_truth"] <= 1
     q2 = q.copy()
     q2[3, 5] = q2[3, 5] ^ 0x04                     # four steps away
-    _, par2 = bench.cpu_baseline(wl, q2, s, min_s=0.0, max_s=60.0, chunk=16, mirror_tokens=24)
+    _, par2 = bench.cpu_baseline(wl, q2, s, min_s=0.0, max_s=60.0, chunk=16, mirror_tokens=24,
+                                 threads=1)
     assert par2["code_mismatches_vs_mirror"] == 1
     assert par2["max_code_steps_vs_truth"] >= 3
 
@@ -116,3 +118,17 @@ def test_e4m3_step_distance():
     a = np.array([0x00, 0x80, 0x01, 0x81, 0x7E, 0x38], np.uint8)
     b = np.array([0x80, 0x00, 0x81, 0x01, 0x7D, 0x3A], np.uint8)
     assert bench.e4m3_steps(a, b).tolist() == [0, 0, 2, 2, 1, 2]
+
+
+def test_cpu_leg_on_a_thread_pool():
+    """With threads > 1 the value is the thread pool's rate, cores its thread
+    count, and the one-thread rate is kept beside it."""
+    wl = W.make_workload(32, 1024, 16, 8, rsf=2.5, seed=4)
+    base, par = bench.cpu_baseline(wl, min_s=0.0, max_s=60.0, chunk=8, threads=3,
+                                   min_s_threads=0.0)
+    assert par is None
+    assert base["cores"] == 3 and base["kind"] == "oracle" and base["unit"] == "GB/s"
+    assert base["value"] > 0 and base["single_thread"]["cores"] == 1
+    assert base["single_thread"]["value"] > 0
+    assert "3 threads" in base["sample"]
+    assert 1 <= bench.host_threads() <= 16
