@@ -450,7 +450,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the shape sweep, the T curve and the same-session ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -541,17 +542,18 @@ def main():
                                          f"timed launches, divided by {args.steps}",
                      "algorithmic_bytes_per_launch": nbytes},
     }
-    read_gbs, copy_gbs, torch_copy_gbs = ceilings(torch)
-    log(f"same-session ceilings: read {read_gbs:.0f}, copy {copy_gbs:.0f}, torch copy "
-        f"{torch_copy_gbs:.0f} GB/s")
-    result["ceilings"] = {
-        "read_gbs": round(read_gbs, 1), "copy_gbs": round(copy_gbs, 1),
-        "torch_copy_gbs": round(torch_copy_gbs, 1),
-        "method": "1 GiB streams after the timed launches: the read and copy probes "
-                  "(moe_bandwidth_probes.h), 10 launches per event pair, median of 5; "
-                  "torch's device copy, median of 20",
-        "headline_frac_of_read": round(achieved / read_gbs, 4),
-        "headline_frac_of_copy": round(achieved / copy_gbs, 4)}
+    if not args.no_sweep:
+        read_gbs, copy_gbs, torch_copy_gbs = ceilings(torch)
+        log(f"same-session ceilings: read {read_gbs:.0f}, copy {copy_gbs:.0f}, torch copy "
+            f"{torch_copy_gbs:.0f} GB/s")
+        result["ceilings"] = {
+            "read_gbs": round(read_gbs, 1), "copy_gbs": round(copy_gbs, 1),
+            "torch_copy_gbs": round(torch_copy_gbs, 1),
+            "method": "1 GiB streams after the timed launches: the read and copy probes "
+                      "(moe_bandwidth_probes.h), 10 launches per event pair, median of 5; "
+                      "torch's device copy, median of 20",
+            "headline_frac_of_read": round(achieved / read_gbs, 4),
+            "headline_frac_of_copy": round(achieved / copy_gbs, 4)}
     # us/call of the same operation on the first T tokens of the same workload,
     # T = 1, 2, 4, ..., 8192, per call under HIP-graph replay
     curve = {}
