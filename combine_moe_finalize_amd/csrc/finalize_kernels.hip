@@ -403,11 +403,17 @@ hipError_t launch_finalize_quant(const Routed& r, uint8_t* out_e4m3, uint8_t* sc
                                  hipStream_t stream) {
   const GatherArgs a = make_args(r);
   u32x2* q = reinterpret_cast<u32x2*>(out_e4m3);
+  // Large launches reserve LDS (unused by the kernel) to hold 4 workgroups
+  // per CU instead of 8: measured 1-2% faster from about a thousand tokens
+  // at H = 7168 (T = 8192: 181.9-182.5 against 185.3-185.7 us), slower for a
+  // grid that would otherwise fit on the chip in one round.
+  const size_t lds = (int64_t)a.tokens * a.nchunks >= kQuantCapFromUnits
+                         ? lds_for_blocks_per_cu(kQuantCapBlocksPerCu) : 0;
   return dispatch_top_k(a.k, [&](auto km, auto ex) {
     constexpr int KM = decltype(km)::value;
     constexpr bool EX = decltype(ex)::value;
     hipLaunchKernelGGL((finalize_quant_kernel<KM, EX>), dim3(plain_blocks(a)),
-                       dim3(kWavesPerBlock * kWaveLanes), 0, stream, a, q, scale_e8m0);
+                       dim3(kWavesPerBlock * kWaveLanes), lds, stream, a, q, scale_e8m0);
     return hipGetLastError();
   });
 }

@@ -66,6 +66,23 @@ constexpr int kNormMaxThreads = 1024;                  // RMSNorm: one block per
 constexpr int kNormMaxChunks = MOEF_MAX_HIDDEN_RMSNORM / (kVecElems * kWaveLanes);
 constexpr int64_t kNormHalfWidthFrom = 1024;           // tokens: half-width RMSNorm blocks
 constexpr int64_t kActQuantPairFrom = int64_t(1) << 21;  // act quant: 2 vectors per lane
+// Occupancy cap for large launches: a launch may reserve LDS it does not use
+// so that at most `blocks` workgroups are resident on a CU at once (gfx950:
+// 160 KiB of LDS per CU). Returns the bytes to reserve: `blocks` workgroups
+// fit, one more does not.
+constexpr int kLdsPerCu = 160 * 1024;
+constexpr size_t lds_for_blocks_per_cu(int blocks) {
+  return (size_t)((kLdsPerCu / (blocks + 1) + 512) / 512 * 512);
+}
+// The quant epilogue holds at most 4 workgroups (16 waves) per CU once its
+// grid is twice what fits on the chip uncapped (16384 (token, chunk) waves):
+// fewer waves streaming at once lose less to reads and writes mixing at the
+// DRAM.
+constexpr int kQuantCapBlocksPerCu = 4;
+constexpr int64_t kQuantCapFromUnits = 16384;
+static_assert(lds_for_blocks_per_cu(kQuantCapBlocksPerCu) * kQuantCapBlocksPerCu <= kLdsPerCu &&
+              lds_for_blocks_per_cu(kQuantCapBlocksPerCu) * (kQuantCapBlocksPerCu + 1) > kLdsPerCu &&
+              lds_for_blocks_per_cu(kQuantCapBlocksPerCu) <= 65536, "cap reservation");
 constexpr int64_t kMaxUnits = (int64_t(1) << 31) - 1;  // (token, chunk) pairs
 
 }  // namespace moef
