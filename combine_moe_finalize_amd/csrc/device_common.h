@@ -46,10 +46,25 @@ __device__ __forceinline__ u32x4 pack8_rne(const float x[8]) {
   return v;
 }
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_fadd(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                           false));
+}
+
+// Sum over the wave, uniform, in a fixed order and without LDS traffic: each
+// 16-lane row by four DPP rotate-and-add steps, then row_bcast:15 and
+// row_bcast:31 add the row sums into the last row, and lane 63 holds the
+// total (the other rows are left partial and are not read).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+  v = dpp_fadd<0x128, 0xF>(v);   // row_ror:8
+  v = dpp_fadd<0x124, 0xF>(v);   // row_ror:4
+  v = dpp_fadd<0x122, 0xF>(v);   // row_ror:2
+  v = dpp_fadd<0x121, 0xF>(v);   // row_ror:1
+  v = dpp_fadd<0x142, 0xA>(v);   // row_bcast:15
+  v = dpp_fadd<0x143, 0xC>(v);   // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // ---------------------------------------------------- RMSNorm of one row

@@ -381,6 +381,11 @@ hipError_t launch_finalize_rmsnorm(const Routed& r, const uint16_t* residual,
   if (a.tokens >= kNormHalfWidthFrom && a.nchunks % 2 == 0) threads /= 2;
   if (threads > kNormMaxThreads) threads = kNormMaxThreads;
   const int cpt = (a.h8 + threads - 1) / threads;   // 1 or 2 (hidden <= 16384)
+  // Two vectors per lane: reserve LDS (unused by the kernel) so that at most
+  // kNorm2MaxWavesPerCu waves are resident per CU; a workgroup too large for
+  // two to fit needs no reservation.
+  const int norm2_blocks = kNorm2MaxWavesPerCu / (threads / kWaveLanes);
+  const size_t lds2 = norm2_blocks >= 2 ? lds_for_blocks_per_cu(norm2_blocks) : 0;
   const float inv_hidden = 1.0f / (float)r.hidden;
   const u32x4* res = reinterpret_cast<const u32x4*>(residual);
   const u32x4* gam = reinterpret_cast<const u32x4*>(gamma);
@@ -394,7 +399,7 @@ hipError_t launch_finalize_rmsnorm(const Routed& r, const uint16_t* residual,
                          0, stream, a, res, gam, eps, inv_hidden, ro, nm);
     else
       hipLaunchKernelGGL((finalize_rmsnorm_kernel<KM, EX, 2>), dim3(a.tokens), dim3(threads),
-                         0, stream, a, res, gam, eps, inv_hidden, ro, nm);
+                         lds2, stream, a, res, gam, eps, inv_hidden, ro, nm);
     return hipGetLastError();
   });
 }

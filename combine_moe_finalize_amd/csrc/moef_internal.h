@@ -80,6 +80,10 @@ constexpr size_t lds_for_blocks_per_cu(int blocks) {
 // DRAM.
 constexpr int kQuantCapBlocksPerCu = 4;
 constexpr int64_t kQuantCapFromUnits = 16384;
+// The RMSNorm epilogue with two column vectors per lane holds at most 20
+// waves per CU (5 per SIMD): measured faster at large T than the 24 its
+// register use would allow.
+constexpr int kNorm2MaxWavesPerCu = 20;
 static_assert(lds_for_blocks_per_cu(kQuantCapBlocksPerCu) * kQuantCapBlocksPerCu <= kLdsPerCu &&
               lds_for_blocks_per_cu(kQuantCapBlocksPerCu) * (kQuantCapBlocksPerCu + 1) > kLdsPerCu &&
               lds_for_blocks_per_cu(kQuantCapBlocksPerCu) <= 65536, "cap reservation");

@@ -92,10 +92,7 @@ topk_sigmoid_gate_kernel(const float* __restrict__ logits, int tokens, int exper
 
   const float my_v = key_value(my_key);
   const float s = lane < k ? 1.0f / (1.0f + expf(-my_v)) : 0.0f;
-  float sum = s;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
-  sum = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sum)));
+  const float sum = wave_sum(s);
   if (lane < k) {
     const float w = s / sum;
     const int64_t o = (int64_t)t * k + lane;
