@@ -360,11 +360,12 @@ unsigned int plain_blocks(const GatherArgs& a) {
 hipError_t launch_finalize(const Routed& r, uint16_t* out, hipStream_t stream) {
   const GatherArgs a = make_args(r);
   u32x4* o = reinterpret_cast<u32x4*>(out);
+  const size_t lds = stream_cap_lds((int64_t)a.tokens * a.nchunks);
   return dispatch_top_k(a.k, [&](auto km, auto ex) {
     constexpr int KM = decltype(km)::value;
     constexpr bool EX = decltype(ex)::value;
     hipLaunchKernelGGL((finalize_kernel<KM, EX>), dim3(plain_blocks(a)),
-                       dim3(kWavesPerBlock * kWaveLanes), 0, stream, a, o);
+                       dim3(kWavesPerBlock * kWaveLanes), lds, stream, a, o);
     return hipGetLastError();
   });
 }
@@ -412,8 +413,7 @@ hipError_t launch_finalize_quant(const Routed& r, uint8_t* out_e4m3, uint8_t* sc
   // per CU instead of 8: measured 1-2% faster from about a thousand tokens
   // at H = 7168 (T = 8192: 181.9-182.5 against 185.3-185.7 us), slower for a
   // grid that would otherwise fit on the chip in one round.
-  const size_t lds = (int64_t)a.tokens * a.nchunks >= kQuantCapFromUnits
-                         ? lds_for_blocks_per_cu(kQuantCapBlocksPerCu) : 0;
+  const size_t lds = stream_cap_lds((int64_t)a.tokens * a.nchunks);
   return dispatch_top_k(a.k, [&](auto km, auto ex) {
     constexpr int KM = decltype(km)::value;
     constexpr bool EX = decltype(ex)::value;
@@ -428,7 +428,8 @@ hipError_t launch_ep_combine(const uint16_t* partials, int32_t num_partials,
                              int64_t hidden, hipStream_t stream) {
   const int64_t n = tokens * (hidden / kVecElems);
   const unsigned int blocks = (unsigned int)((n + 255) / 256);
-  hipLaunchKernelGGL(ep_combine_kernel, dim3(blocks), dim3(256), 0, stream,
+  const size_t lds = stream_cap_lds(((int64_t)blocks * 256) / kWaveLanes);
+  hipLaunchKernelGGL(ep_combine_kernel, dim3(blocks), dim3(256), lds, stream,
                      reinterpret_cast<const u32x4*>(partials), (int)num_partials, n,
                      reinterpret_cast<const u32x4*>(shared), reinterpret_cast<u32x4*>(out), n);
   return hipGetLastError();

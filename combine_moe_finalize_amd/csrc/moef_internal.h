@@ -74,19 +74,23 @@ constexpr int kLdsPerCu = 160 * 1024;
 constexpr size_t lds_for_blocks_per_cu(int blocks) {
   return (size_t)((kLdsPerCu / (blocks + 1) + 512) / 512 * 512);
 }
-// The quant epilogue holds at most 4 workgroups (16 waves) per CU once its
-// grid is twice what fits on the chip uncapped (16384 (token, chunk) waves):
-// fewer waves streaming at once lose less to reads and writes mixing at the
-// DRAM.
-constexpr int kQuantCapBlocksPerCu = 4;
-constexpr int64_t kQuantCapFromUnits = 16384;
+// The finalize kernels with one wave per (token, chunk) and the EP combine
+// hold at most 4 of their 4-wave workgroups (16 waves) per CU once a grid is
+// twice what fits on the chip uncapped (16384 waves): fewer waves streaming
+// at once lose less to reads and writes mixing at the DRAM. (The act-quant
+// kernels measured slower with any cap and run uncapped.)
+constexpr int kStreamCapBlocksPerCu = 4;
+constexpr int64_t kStreamCapFromWaves = 16384;
+constexpr size_t stream_cap_lds(int64_t waves) {
+  return waves >= kStreamCapFromWaves ? lds_for_blocks_per_cu(kStreamCapBlocksPerCu) : 0;
+}
 // The RMSNorm epilogue with two column vectors per lane holds at most 20
 // waves per CU (5 per SIMD): measured faster at large T than the 24 its
 // register use would allow.
 constexpr int kNorm2MaxWavesPerCu = 20;
-static_assert(lds_for_blocks_per_cu(kQuantCapBlocksPerCu) * kQuantCapBlocksPerCu <= kLdsPerCu &&
-              lds_for_blocks_per_cu(kQuantCapBlocksPerCu) * (kQuantCapBlocksPerCu + 1) > kLdsPerCu &&
-              lds_for_blocks_per_cu(kQuantCapBlocksPerCu) <= 65536, "cap reservation");
+static_assert(lds_for_blocks_per_cu(kStreamCapBlocksPerCu) * kStreamCapBlocksPerCu <= kLdsPerCu &&
+              lds_for_blocks_per_cu(kStreamCapBlocksPerCu) * (kStreamCapBlocksPerCu + 1) > kLdsPerCu &&
+              lds_for_blocks_per_cu(kStreamCapBlocksPerCu) <= 65536, "cap reservation");
 constexpr int64_t kMaxUnits = (int64_t(1) << 31) - 1;  // (token, chunk) pairs
 
 }  // namespace moef
