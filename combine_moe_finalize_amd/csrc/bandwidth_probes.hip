@@ -45,9 +45,11 @@ copy_probe_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst) {
   for (int u = 0; u < kPerLane; ++u) __builtin_nontemporal_store(v[u], dst + base + u * kThreads);
 }
 
+// A dispatch packet counts a grid's work-items in 32 bits: at most
+// (2^32 - 1) / 256 workgroups of 256 lanes, one grain each.
 bool grain_count_ok(int64_t bytes) {
   return bytes > 0 && bytes % MOEF_PROBE_GRAIN == 0 &&
-         bytes / MOEF_PROBE_GRAIN <= (int64_t)INT32_MAX;
+         bytes / MOEF_PROBE_GRAIN <= MOEF_PROBE_MAX_GRAINS;
 }
 
 bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }

@@ -253,7 +253,9 @@ int moe_finalize_ep_combine(const uint16_t* partials, int32_t num_partials,
   if (num_tokens < 0 || hidden < 1 || num_partials < 1 || num_partials > MOEF_MAX_EP_PARTIALS)
     return MOEF_ERR_BAD_SHAPE;
   if (hidden % moef::kVecElems != 0 || hidden > MOEF_MAX_HIDDEN) return MOEF_ERR_UNSUPPORTED;
-  if (num_tokens * (hidden / moef::kVecElems) > moef::kMaxUnits * 256) return MOEF_ERR_UNSUPPORTED;
+  if (num_tokens > moef::kMaxGridItems ||
+      num_tokens * (hidden / moef::kVecElems) > moef::kMaxGridItems)
+    return MOEF_ERR_UNSUPPORTED;
   if (num_tokens == 0) return MOEF_OK;
   if (partials == nullptr || out == nullptr) return MOEF_ERR_NULL_POINTER;
   if (!aligned(partials, 16) || !aligned(shared_out, 16) || !aligned(out, 16))
@@ -272,7 +274,9 @@ int moe_allreduce_residual_rmsnorm(const uint16_t* const* rank_outputs, int32_t 
   if (num_tokens < 0 || hidden < 1 || num_ranks < 1 || num_ranks > MOEF_MAX_AR_RANKS)
     return MOEF_ERR_BAD_SHAPE;
   if (hidden % moef::kVecElems != 0 || hidden > MOEF_MAX_HIDDEN_RMSNORM ||
-      num_tokens > moef::kMaxUnits)
+      num_tokens > moef::kMaxUnits ||
+      num_tokens * ((hidden / moef::kVecElems + moef::kWaveLanes - 1) / moef::kWaveLanes) >
+          moef::kMaxUnits)
     return MOEF_ERR_UNSUPPORTED;
   if (num_tokens == 0) return MOEF_OK;
   if (rank_outputs == nullptr || residual == nullptr || gamma == nullptr ||
@@ -304,7 +308,7 @@ int moe_allreduce_residual_rmsnorm(const uint16_t* const* rank_outputs, int32_t 
 int moe_topk_packed_decode(const int32_t* packed, int64_t n, int32_t* expert_ids,
                            float* weights, void* stream) {
   if (n < 0) return MOEF_ERR_BAD_SHAPE;
-  if (n > moef::kMaxUnits * 256) return MOEF_ERR_UNSUPPORTED;
+  if (n > moef::kMaxGridItems) return MOEF_ERR_UNSUPPORTED;
   if (n == 0) return MOEF_OK;
   if (packed == nullptr || (expert_ids == nullptr && weights == nullptr))
     return MOEF_ERR_NULL_POINTER;
@@ -325,7 +329,7 @@ int moe_topk_sigmoid_gate(const float* router_logits, int64_t num_tokens, int32_
       top_k > num_experts)
     return MOEF_ERR_BAD_SHAPE;
   if (num_experts > MOEF_MAX_GATE_EXPERTS) return MOEF_ERR_UNSUPPORTED;
-  if (num_tokens > (int64_t)INT32_MAX - 4) return MOEF_ERR_UNSUPPORTED;
+  if (num_tokens > moef::kMaxUnits) return MOEF_ERR_UNSUPPORTED;   // one wave per token
   if (num_tokens == 0) return MOEF_OK;
   if (router_logits == nullptr || topk_ids == nullptr) return MOEF_ERR_NULL_POINTER;
   if (!aligned(router_logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||

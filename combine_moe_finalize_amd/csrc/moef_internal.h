@@ -91,6 +91,14 @@ constexpr int kNorm2MaxWavesPerCu = 20;
 static_assert(lds_for_blocks_per_cu(kStreamCapBlocksPerCu) * kStreamCapBlocksPerCu <= kLdsPerCu &&
               lds_for_blocks_per_cu(kStreamCapBlocksPerCu) * (kStreamCapBlocksPerCu + 1) > kLdsPerCu &&
               lds_for_blocks_per_cu(kStreamCapBlocksPerCu) <= 65536, "cap reservation");
-constexpr int64_t kMaxUnits = (int64_t(1) << 31) - 1;  // (token, chunk) pairs
+// A kernel dispatch packet states a 1-D grid's size in work-items in a 32-bit
+// field, so one launch holds at most 2^32 - 1 work-items. kMaxGridItems is the
+// largest multiple of 256 (every rounded-up grid here uses 256-lane
+// workgroups) below that; a grid of at most kMaxUnits one-wave units, or of
+// kMaxGridItems single-lane items, rounded up to whole workgroups, fits.
+constexpr int64_t kMaxGridItems = (int64_t(1) << 32) - 256;
+constexpr int64_t kMaxUnits = kMaxGridItems / kWaveLanes;   // 2^26 - 4 (token, chunk) pairs
+static_assert(kMaxUnits % kWavesPerBlock == 0, "whole 4-wave workgroups");
+static_assert(kMaxUnits == MOEF_MAX_UNITS && kMaxGridItems == MOEF_MAX_ITEMS, "header limits");
 
 }  // namespace moef

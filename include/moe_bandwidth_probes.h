@@ -9,7 +9,9 @@
  * loads, each lane keeping four loads in flight; one workgroup covers 16 KiB.
  *
  *  src, dst  device pointers, 16-byte aligned, `bytes` long each.
- *  bytes     a positive multiple of MOEF_PROBE_GRAIN.
+ *  bytes     a positive multiple of MOEF_PROBE_GRAIN, at most
+ *            MOEF_PROBE_MAX_GRAINS of them (one launch covers at most
+ *            2^32 - 1 work-items, 256 per grain).
  *  sink      device uint32 (read probe): written only when the XOR of a
  *            lane's 64 bytes equals 0x9E3779B9, which keeps the loads from
  *            being optimized away; with all-zero input it is never written.
@@ -17,9 +19,9 @@
  *            without waiting.
  *
  * Return value: 0, or 1 (a NULL pointer), 2 (bytes not a positive multiple
- * of MOEF_PROBE_GRAIN, or more than 2^31 - 1 grains), 4 (src or dst not
- * 16-byte aligned, sink not 4-byte aligned), 6 (dst overlaps src), 7 (the
- * HIP runtime rejected the launch). Checks run before any HIP call.
+ * of MOEF_PROBE_GRAIN, or more than MOEF_PROBE_MAX_GRAINS grains), 4 (src or
+ * dst not 16-byte aligned, sink not 4-byte aligned), 6 (dst overlaps src),
+ * 7 (the HIP runtime rejected the launch). Checks run before any HIP call.
  */
 #ifndef MOE_BANDWIDTH_PROBES_H
 #define MOE_BANDWIDTH_PROBES_H
@@ -31,6 +33,7 @@ extern "C" {
 #endif
 
 #define MOEF_PROBE_GRAIN 16384
+#define MOEF_PROBE_MAX_GRAINS 16777215LL /* 2^24 - 1 */
 
 /* Reads every byte of src once. */
 int moef_probe_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);

@@ -88,6 +88,14 @@ extern "C" {
 #define MOEF_MAX_GATE_EXPERTS 512    /* the gate keeps a token's logits in registers */
 #define MOEF_MAX_EP_PARTIALS 64      /* partials one combine call may sum */
 #define MOEF_MAX_AR_RANKS 16         /* rank outputs one all-reduce call may sum */
+/* Launch-size limits. A kernel dispatch packet counts a grid's work-items in
+ * 32 bits, so one launch covers at most 2^32 - 1 of them. A call may therefore
+ * hold at most MOEF_MAX_UNITS one-wave units (a token's 512-column chunk, or
+ * one token of the gate) or MOEF_MAX_ITEMS one-lane items (16-byte vectors of
+ * the combine, words of the decoder); beyond them it returns
+ * MOEF_ERR_UNSUPPORTED. */
+#define MOEF_MAX_UNITS 67108860LL    /* 2^26 - 4 */
+#define MOEF_MAX_ITEMS 4294967040LL  /* 2^32 - 256 */
 
 #define MOEF_DEVERR_INDEX_OUT_OF_RANGE 1
 
@@ -121,8 +129,8 @@ enum moef_status {
  *  out         bf16 [num_tokens, hidden], written.
  *  err_flag    optional device int32 (see conventions).
  *  num_tokens, hidden, top_k  shape rules of the conventions, and
- *              num_tokens * ceil(hidden / 512) <= 2^31 - 1 (one wave per
- *              512-column chunk of a token), else MOEF_ERR_UNSUPPORTED.
+ *              num_tokens * ceil(hidden / 512) <= MOEF_MAX_UNITS (one wave
+ *              per 512-column chunk of a token), else MOEF_ERR_UNSUPPORTED.
  */
 int moe_finalize(const uint16_t* gemm2_out, int64_t num_rows,
                  const int32_t* expanded_idx_to_permuted_idx,
@@ -204,7 +212,7 @@ int moe_finalize_quant_ue8m0(const uint16_t* gemm2_out, int64_t num_rows,
  *  hidden       a multiple of 8. num_tokens == 0 is a no-op.
  *  Errors: num_tokens < 0, hidden < 1 or num_partials outside
  *  [1, MOEF_MAX_EP_PARTIALS] give BAD_SHAPE; hidden not a multiple of 8 or
- *  above MOEF_MAX_HIDDEN, or num_tokens * hidden / 8 above (2^31 - 1) * 256,
+ *  above MOEF_MAX_HIDDEN, or num_tokens * hidden / 8 above MOEF_MAX_ITEMS,
  *  give UNSUPPORTED; a NULL partials or out gives NULL_POINTER; a pointer
  *  that is not 16-byte aligned gives MISALIGNED; out overlapping the partials
  *  or shared_out gives BAD_ALIAS.
@@ -243,7 +251,7 @@ int moe_finalize_ep_combine(const uint16_t* partials, int32_t num_partials,
  *  num_tokens == 0 is a no-op.
  *  Errors: R outside [1, MOEF_MAX_AR_RANKS], num_tokens < 0 or hidden < 1
  *  give BAD_SHAPE; hidden not a multiple of 8, hidden above the limit or
- *  num_tokens above 2^31 - 1 give UNSUPPORTED; a NULL array, rank pointer or
+ *  num_tokens * ceil(hidden / 512) above MOEF_MAX_UNITS give UNSUPPORTED; a NULL array, rank pointer or
  *  buffer gives NULL_POINTER; a pointer that is not 16-byte aligned gives
  *  MISALIGNED; the overlaps above give BAD_ALIAS.
  */
@@ -261,7 +269,7 @@ int moe_allreduce_residual_rmsnorm(const uint16_t* const* rank_outputs, int32_t 
  *  expert_ids  int32 [n] = (uint32)packed >> 16, or NULL to skip.
  *  weights     float32 [n] = the bf16 weight widened exactly, or NULL.
  *  At least one output must be non-NULL. n == 0 is a no-op.
- *  Errors: n < 0 gives BAD_SHAPE; n above (2^31 - 1) * 256 gives UNSUPPORTED;
+ *  Errors: n < 0 gives BAD_SHAPE; n above MOEF_MAX_ITEMS gives UNSUPPORTED;
  *  a NULL packed, or both outputs NULL, gives NULL_POINTER; a pointer that is
  *  not 4-byte aligned gives MISALIGNED; an output that overlaps packed or the
  *  other output gives BAD_ALIAS.
@@ -290,7 +298,7 @@ int moe_topk_packed_decode(const int32_t* packed, int64_t n,
  *  num_tokens == 0 is a no-op.
  *  Errors: num_tokens < 0, num_experts < 1 or top_k outside [1, min(E, 16)]
  *  give BAD_SHAPE; num_experts above MOEF_MAX_GATE_EXPERTS or num_tokens
- *  above 2^31 - 5 give UNSUPPORTED; a NULL router_logits or topk_ids gives
+ *  above MOEF_MAX_UNITS give UNSUPPORTED; a NULL router_logits or topk_ids gives
  *  NULL_POINTER; a pointer that is not 4-byte aligned gives MISALIGNED; an
  *  output that overlaps the logits or another output gives BAD_ALIAS.
  */
@@ -319,8 +327,8 @@ int moe_topk_sigmoid_gate(const float* router_logits, int64_t num_tokens,
  *              codes = e4m3(fp32(x / scale)), nearest even.
  *  num_tokens == 0 is a no-op.
  *  Errors: num_tokens < 0 or hidden < 1 give BAD_SHAPE; hidden not a
- *  multiple of 128 or above MOEF_MAX_HIDDEN, num_tokens above 2^31 - 1, or
- *  num_tokens * ceil(hidden / 512) above 2^31 - 1 give UNSUPPORTED; a NULL x,
+ *  multiple of 128 or above MOEF_MAX_HIDDEN, or num_tokens * ceil(hidden /
+ *  512) above MOEF_MAX_UNITS give UNSUPPORTED; a NULL x,
  *  out_e4m3 or scale gives NULL_POINTER (a NULL scale is reported before the
  *  shape checks when num_tokens > 0); x not 16-, out_e4m3 not 8- or
  *  scale_f32 not 4-byte aligned gives MISALIGNED; an output that overlaps x

@@ -40,17 +40,24 @@ int main() {
                                            at<int32_t>(PK), nullptr, 1.0f, at<uint16_t>(OUT), 1,
                                            8, 1, nullptr, nullptr), MOEF_OK, true);
   // largest accepted sizes: gemm2_out spans 2^31 rows of 2 MiB (4.5e15 bytes),
-  // so the other buffers sit below it, apart from each other
+  // so the other buffers sit below it, apart from each other; 32767 tokens of
+  // 2048 chunks are the most whole tokens of 2^20 columns MOEF_MAX_UNITS allows
   check("finalize largest sizes", moe_finalize(at<uint16_t>(0x10000000000000ull), INT32_MAX,
                                                at<int32_t>(0x30000000000ull),
                                                at<float>(0x40000000000ull), nullptr, nullptr, 1.0f,
-                                               at<uint16_t>(0x1000), (1 << 20) - 1, 1 << 20, 16,
+                                               at<uint16_t>(0x1000), 32767, 1 << 20, 16,
                                                nullptr, nullptr),
         MOEF_OK, true);
-  check("finalize exactly 2^31 units", moe_finalize(at<uint16_t>(G2), 1, at<int32_t>(IDX),
-                                                    at<float>(W), nullptr, nullptr, 1.0f,
-                                                    at<uint16_t>(0x7f0000000000ull), 1 << 20,
-                                                    1 << 20, 1, nullptr, nullptr),
+  check("finalize 32768 tokens of 2^20 columns", moe_finalize(
+      at<uint16_t>(0x10000000000000ull), INT32_MAX, at<int32_t>(0x30000000000ull),
+      at<float>(0x40000000000ull), nullptr, nullptr, 1.0f, at<uint16_t>(0x1000), 32768, 1 << 20,
+      16, nullptr, nullptr), MOEF_ERR_UNSUPPORTED, false);
+  check("finalize MOEF_MAX_UNITS one-chunk tokens", moe_finalize(
+      at<uint16_t>(G2), 1, at<int32_t>(IDX), at<float>(W), nullptr, nullptr, 1.0f,
+      at<uint16_t>(0x7f0000000000ull), MOEF_MAX_UNITS, 512, 1, nullptr, nullptr), MOEF_OK, true);
+  check("finalize one unit beyond MOEF_MAX_UNITS", moe_finalize(
+      at<uint16_t>(G2), 1, at<int32_t>(IDX), at<float>(W), nullptr, nullptr, 1.0f,
+      at<uint16_t>(0x7f0000000000ull), MOEF_MAX_UNITS + 1, 512, 1, nullptr, nullptr),
         MOEF_ERR_UNSUPPORTED, false);
   check("finalize units beyond 2^31", moe_finalize(at<uint16_t>(G2), 1, at<int32_t>(IDX),
                                                    at<float>(W), nullptr, nullptr, 1.0f,
@@ -116,10 +123,23 @@ int main() {
                                             at<float>(W), nullptr), MOEF_OK, true);
   check("decode n huge", moe_topk_packed_decode(at<int32_t>(PK), INT64_MAX, at<int32_t>(IDX),
                                                 at<float>(W), nullptr), MOEF_ERR_UNSUPPORTED, false);
+  check("decode MOEF_MAX_ITEMS", moe_topk_packed_decode(at<int32_t>(PK), MOEF_MAX_ITEMS,
+                                                        at<int32_t>(IDX), at<float>(W), nullptr),
+        MOEF_OK, true);
+  check("decode MOEF_MAX_ITEMS + 1", moe_topk_packed_decode(at<int32_t>(PK), MOEF_MAX_ITEMS + 1,
+                                                            at<int32_t>(IDX), at<float>(W),
+                                                            nullptr),
+        MOEF_ERR_UNSUPPORTED, false);
   check("gate ok", moe_topk_sigmoid_gate(at<float>(G2), 8192, 256, 8, at<int32_t>(IDX),
                                          at<float>(W), at<int32_t>(PK), nullptr), MOEF_OK, true);
   check("gate T huge", moe_topk_sigmoid_gate(at<float>(G2), INT64_MAX, 256, 8, at<int32_t>(IDX),
                                              nullptr, nullptr, nullptr), MOEF_ERR_UNSUPPORTED, false);
+  check("gate MOEF_MAX_UNITS tokens", moe_topk_sigmoid_gate(at<float>(G2), MOEF_MAX_UNITS, 1, 1,
+                                                            at<int32_t>(IDX), nullptr, nullptr,
+                                                            nullptr), MOEF_OK, true);
+  check("gate MOEF_MAX_UNITS + 1 tokens", moe_topk_sigmoid_gate(
+      at<float>(G2), MOEF_MAX_UNITS + 1, 1, 1, at<int32_t>(IDX), nullptr, nullptr, nullptr),
+        MOEF_ERR_UNSUPPORTED, false);
   check("act quant ue8m0 ok", moe_act_quant_fp8_ue8m0(at<uint16_t>(G2), 8192, 7168, at<uint8_t>(Q),
                                                       at<uint8_t>(S), nullptr), MOEF_OK, true);
   check("act quant amax ok", moe_act_quant_fp8_amax(at<uint16_t>(G2), 8192, 7168, at<uint8_t>(Q),
@@ -127,14 +147,26 @@ int main() {
   check("act quant H huge", moe_act_quant_fp8_amax(at<uint16_t>(G2), 1, INT64_MAX - 127,
                                                    at<uint8_t>(Q), at<float>(S), nullptr),
         MOEF_ERR_UNSUPPORTED, false);
+  check("act quant MOEF_MAX_UNITS chunks", moe_act_quant_fp8_ue8m0(
+      at<uint16_t>(0x100000000000ull), MOEF_MAX_UNITS, 512, at<uint8_t>(0x300000000000ull),
+      at<uint8_t>(0x400000000000ull), nullptr), MOEF_OK, true);
+  check("act quant MOEF_MAX_UNITS + 1 chunks", moe_act_quant_fp8_ue8m0(
+      at<uint16_t>(0x100000000000ull), MOEF_MAX_UNITS + 1, 512, at<uint8_t>(0x300000000000ull),
+      at<uint8_t>(0x400000000000ull), nullptr), MOEF_ERR_UNSUPPORTED, false);
   check("ep combine ok", moe_finalize_ep_combine(at<uint16_t>(G2), 4, at<uint16_t>(SH),
                                                  at<uint16_t>(OUT), 8192, 7168, nullptr),
         MOEF_OK, true);
   check("ep combine T huge", moe_finalize_ep_combine(at<uint16_t>(G2), 4, nullptr,
                                                      at<uint16_t>(OUT), INT64_MAX, 8, nullptr),
         MOEF_ERR_UNSUPPORTED, false);
+  check("ep combine MOEF_MAX_ITEMS vectors", moe_finalize_ep_combine(
+      at<uint16_t>(0x100000000000ull), 2, nullptr, at<uint16_t>(0x300000000000ull),
+      MOEF_MAX_ITEMS / 16, 128, nullptr), MOEF_OK, true);
+  check("ep combine MOEF_MAX_ITEMS + 16 vectors", moe_finalize_ep_combine(
+      at<uint16_t>(0x100000000000ull), 2, nullptr, at<uint16_t>(0x300000000000ull),
+      MOEF_MAX_ITEMS / 16 + 1, 128, nullptr), MOEF_ERR_UNSUPPORTED, false);
   // all-reduce + residual + RMSNorm: rank buffers 2^46 bytes apart hold the
-  // largest accepted size (2^31 - 1 tokens of 16384 columns)
+  // largest accepted size (MOEF_MAX_UNITS / 32 tokens of 16384 columns)
   {
     const uint16_t* ranks[MOEF_MAX_AR_RANKS + 1];
     for (int r = 0; r <= MOEF_MAX_AR_RANKS; ++r)
@@ -147,8 +179,11 @@ int main() {
     check("allreduce ok", moe_allreduce_residual_rmsnorm(ranks, 8, res, gam, 1e-6f, ro, nm, 256,
                                                          7168, nullptr), MOEF_OK, true);
     check("allreduce largest sizes", moe_allreduce_residual_rmsnorm(
-        ranks, MOEF_MAX_AR_RANKS, res, gam, 1e-6f, ro, nm, INT32_MAX, 16384, nullptr),
+        ranks, MOEF_MAX_AR_RANKS, res, gam, 1e-6f, ro, nm, MOEF_MAX_UNITS / 32, 16384, nullptr),
         MOEF_OK, true);
+    check("allreduce one token beyond", moe_allreduce_residual_rmsnorm(
+        ranks, 2, res, gam, 1e-6f, ro, nm, MOEF_MAX_UNITS / 32 + 1, 16384, nullptr),
+        MOEF_ERR_UNSUPPORTED, false);
     check("allreduce in place", moe_allreduce_residual_rmsnorm(ranks, 3, res, gam, 1e-6f, res, nm,
                                                                16, 7168, nullptr), MOEF_OK, true);
     check("allreduce T beyond 2^31 - 1", moe_allreduce_residual_rmsnorm(

@@ -27,6 +27,8 @@ ALL = {OK, NULLP, SHAPE, UNSUP, MISAL, FORMAT, ALIAS}
 MAX_TOP_K, MAX_HIDDEN, MAX_HIDDEN_RMSNORM, QUANT_BLOCK = 16, 1 << 20, 16384, 128
 MAX_GATE_EXPERTS, MAX_EP_PARTIALS, MAX_AR_RANKS = 512, 64, 16
 I32 = 2 ** 31 - 1
+MAX_UNITS = 2 ** 26 - 4      # one-wave units a launch may hold (MOEF_MAX_UNITS)
+MAX_ITEMS = 2 ** 32 - 256    # one-lane items (MOEF_MAX_ITEMS)
 
 vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
 ROUTED = [vp, i64, vp, vp, vp, vp, f32]
@@ -76,7 +78,7 @@ def shape_rules(kind, c):
                 v.add(UNSUP)
             if H > MAX_HIDDEN:
                 v |= {SHAPE, UNSUP}
-            if P > I32 or T > I32 or (T >= 0 and T * chunks(H) > I32):
+            if P > I32 or T > I32 or (T >= 0 and T * chunks(H) > MAX_UNITS):
                 v.add(UNSUP)
             if kind == "rmsnorm" and H > MAX_HIDDEN_RMSNORM:
                 v.add(UNSUP)
@@ -85,32 +87,32 @@ def shape_rules(kind, c):
     elif kind == "decode":
         if c["n"] < 0:
             v.add(SHAPE)
-        if c["n"] > I32 * 256:
+        if c["n"] > MAX_ITEMS:
             v.add(UNSUP)
     elif kind == "gate":
         T, E, k = c["T"], c["E"], c["k"]
         if T < 0 or E < 1 or not 1 <= k <= min(E, MAX_TOP_K):
             v.add(SHAPE)
-        if E > MAX_GATE_EXPERTS or T > I32 - 4:
+        if E > MAX_GATE_EXPERTS or T > MAX_UNITS:
             v.add(UNSUP)
     elif kind in ("aq_ue8m0", "aq_amax"):
         T, H = c["T"], c["H"]
         if T < 0 or H < 1:
             v.add(SHAPE)
-        if H >= 1 and (H % QUANT_BLOCK or H > MAX_HIDDEN or T > I32 or
-                       (T >= 0 and T * chunks(H) > I32)):
+        if H >= 1 and (H % QUANT_BLOCK or H > MAX_HIDDEN or
+                       (T >= 0 and T * chunks(H) > MAX_UNITS)):
             v.add(UNSUP)
     elif kind == "combine":
         T, H, R = c["T"], c["H"], c["R"]
         if T < 0 or H < 1 or not 1 <= R <= MAX_EP_PARTIALS:
             v.add(SHAPE)
-        if H >= 1 and (H % 8 or H > MAX_HIDDEN or (T >= 0 and T * (H // 8) > I32 * 256)):
+        if H >= 1 and (H % 8 or H > MAX_HIDDEN or (T >= 0 and T * (H // 8) > MAX_ITEMS)):
             v.add(UNSUP)
     elif kind == "allreduce":
         T, H, R = c["T"], c["H"], c["R"]
         if T < 0 or H < 1 or not 1 <= R <= MAX_AR_RANKS:
             v.add(SHAPE)
-        if H >= 1 and (H % 8 or H > MAX_HIDDEN_RMSNORM or T > I32):
+        if H >= 1 and (H % 8 or H > MAX_HIDDEN_RMSNORM or (T >= 0 and T * chunks(H) > MAX_UNITS)):
             v.add(UNSUP)
     return v
 
@@ -236,7 +238,8 @@ def draw_count(rng, small=300):
     if r < 0.08:
         return int(rng.choice([-1, -5]))
     if r < 0.11:
-        return int(rng.choice([I32 - 4, I32 - 3, I32, I32 + 1, 1 << 30, 1 << 21]))
+        return int(rng.choice([I32 - 4, I32 - 3, I32, I32 + 1, 1 << 30, 1 << 21, MAX_UNITS,
+                               MAX_UNITS + 1, MAX_UNITS // 14, MAX_UNITS // 14 + 1]))
     return int(rng.integers(1, small))
 
 
@@ -269,7 +272,7 @@ def draw(rng, kind):
     elif kind == "decode":
         c["n"] = draw_count(rng, 5000)
         if rng.random() < 0.03:
-            c["n"] = int(rng.choice([I32 * 256, I32 * 256 + 1]))
+            c["n"] = int(rng.choice([I32 * 256, I32 * 256 + 1, MAX_ITEMS, MAX_ITEMS + 1]))
         names = ["pk", "ids", "w"]
     elif kind == "gate":
         c["T"] = draw_count(rng)
@@ -288,7 +291,7 @@ def draw(rng, kind):
         c["R"] = int(rng.integers(1, 9)) if rng.random() > 0.08 else int(
             rng.choice([0, -1, 64, 65]))
         if c["T"] > 0 and c["H"] > 0 and rng.random() < 0.03:
-            c["T"] = (I32 * 256) // (c["H"] // 8 or 1) + int(rng.integers(0, 2))
+            c["T"] = MAX_ITEMS // (c["H"] // 8 or 1) + int(rng.integers(0, 2))
         names = ["parts", "sh", "out"]
     else:
         c["T"] = draw_count(rng)

@@ -37,7 +37,8 @@ def test_exports_the_header(lib):
 def test_rejections(lib):
     r, c = lib.moef_probe_read, lib.moef_probe_copy
     assert r(None, GRAIN, B, None) == 1 and r(A, GRAIN, None, None) == 1
-    for bad in (0, -GRAIN, GRAIN - 16, GRAIN + 16, GRAIN * (2 ** 31)):
+    # one launch covers at most 2^32 - 1 work-items: 2^24 - 1 grains of 256 lanes
+    for bad in (0, -GRAIN, GRAIN - 16, GRAIN + 16, GRAIN * (2 ** 24), GRAIN * (2 ** 31)):
         assert r(A, bad, B, None) == 2, bad
         assert c(A, B, bad, None) == 2, bad
     assert r(A + 8, GRAIN, B, None) == 4 and r(A, GRAIN, B + 2, None) == 4
