@@ -34,7 +34,11 @@ Printed: one JSON line with
              a 1 GiB buffer through the caches); the sustained per-call time
              of 100 back-to-back calls; and the per-call time of 20 calls
              captured in a HIP graph and replayed. Kernel-only durations come
-             from rocprofv3 (see profiles/).
+             from rocprofv3 (see profiles/),
+  us_per_call  the timed operation on its first T = 1, 2, 4, ..., 8192
+             tokens, the decode finalize at T = 1..256, and an empty kernel
+             (one wave, no memory access), all per call under HIP-graph
+             replay: the empty kernel is the floor under any call's time.
 """
 from __future__ import annotations
 
@@ -52,7 +56,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_moe_finalize_amd", "csrc", f)
-                  for f in ("finalize_kernels.hip", "device_common.h")]
+                  for f in ("finalize_kernels.hip", "device_common.h", "moef_internal.h")]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_quant_T8192_H7168_counters.json")
 
 
@@ -390,6 +394,22 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
     return rows
 
 
+def launch_floor_us(torch):
+    """Per-call time of the probe library's empty kernel (one wave, no memory
+    access) under the same HIP-graph replay as the small calls: the floor
+    under any kernel's time per call."""
+    import ctypes
+    from combine_moe_finalize_amd._paths import PROBE_LIB_PATH
+    P = ctypes.CDLL(PROBE_LIB_PATH)                  # fails loudly when it is not built
+    P.moef_probe_empty.argtypes = [ctypes.c_void_p]
+
+    def launch():
+        if P.moef_probe_empty(torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("empty probe: launch failed")
+
+    return graph_us(torch, launch, 20, reps=5)
+
+
 def ceilings(torch, nbytes=1 << 30):
     """Same-session HBM rates in GB/s: the streaming read and copy probes
     (moe_bandwidth_probes.h) over `nbytes`, 10 back-to-back launches between
@@ -588,7 +608,8 @@ def main():
                     if r["case"] == "decode"}
         result["us_per_call"] = {
             "finalize_quant_ue8m0_H7168_k8_graph_replay": curve,
-            "finalize_H4096_k8_graph_replay": per_call}
+            "finalize_H4096_k8_graph_replay": per_call,
+            "empty_kernel_graph_replay": round(launch_floor_us(torch), 3)}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"], result["parity"] = cpu_baseline(wl, q_host, s_host)

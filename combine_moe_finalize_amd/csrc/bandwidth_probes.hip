@@ -1,5 +1,6 @@
 // gfx950 streaming read and copy kernels: the HBM rates a plain stream
-// reaches, measured beside the finalize kernels in the same session.
+// reaches, measured beside the finalize kernels in the same session; and an
+// empty kernel, the per-launch floor that small calls are compared with.
 //
 // Work layout: one 256-lane workgroup covers 16 KiB, 1024 vectors of 16
 // bytes; lane t of the workgroup takes vectors t, t + 256, t + 512 and
@@ -45,6 +46,9 @@ copy_probe_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst) {
   for (int u = 0; u < kPerLane; ++u) __builtin_nontemporal_store(v[u], dst + base + u * kThreads);
 }
 
+// One wave that does nothing: what a launch costs before any memory access.
+__global__ void __launch_bounds__(64) empty_probe_kernel() {}
+
 // A dispatch packet counts a grid's work-items in 32 bits: at most
 // (2^32 - 1) / 256 workgroups of 256 lanes, one grain each.
 bool grain_count_ok(int64_t bytes) {
@@ -77,6 +81,11 @@ int moef_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned int)(bytes / MOEF_PROBE_GRAIN)),
                      dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst));
+  return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
+int moef_probe_empty(void* stream) {
+  hipLaunchKernelGGL(empty_probe_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream));
   return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 

@@ -2,8 +2,8 @@
  * moe_bandwidth_probes.h - streaming read and copy kernels that measure the
  * HBM rates one MI355X reaches in the same session as a benchmark, so the
  * finalize kernels can be reported against a measured ceiling beside the
- * 8 TB/s specification. Measurement infrastructure: the finalize library does
- * not use them.
+ * 8 TB/s specification, and an empty kernel for the per-launch floor.
+ * Measurement infrastructure: the finalize library does not use them.
  *
  * Both kernels read `bytes` from `src` as 16-byte vectors with non-temporal
  * loads, each lane keeping four loads in flight; one workgroup covers 16 KiB.
@@ -40,6 +40,10 @@ int moef_probe_read(const void* src, int64_t bytes, uint32_t* sink, void* stream
 
 /* dst = src, byte for byte, with non-temporal loads and stores. */
 int moef_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/* One 64-lane workgroup that does nothing: the cost of a launch itself, the
+ * floor under any kernel's time per call. Returns 0, or 7. */
+int moef_probe_empty(void* stream);
 
 #ifdef __cplusplus
 }

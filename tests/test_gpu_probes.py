@@ -1,6 +1,6 @@
-"""The bandwidth probes on the GPU: the copy is byte-exact, and the read
-probe really reads (its sink is written when, and only when, a lane's bytes
-XOR to the sentinel)."""
+"""The bandwidth probes on the GPU: the copy is byte-exact, the read probe
+really reads (its sink is written when, and only when, a lane's bytes XOR to
+the sentinel), and the empty kernel launches."""
 import ctypes
 
 import pytest
@@ -23,7 +23,16 @@ def lib():
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     L.moef_probe_read.argtypes = [vp, i64, vp, vp]
     L.moef_probe_copy.argtypes = [vp, vp, i64, vp]
+    L.moef_probe_empty.argtypes = [vp]
     return L
+
+
+def test_empty_probe_launches(lib):
+    announce("probe empty, 100 launches")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(100):
+        assert lib.moef_probe_empty(stream) == 0
+    torch.cuda.synchronize()
 
 
 def test_copy_is_exact(lib):

@@ -28,7 +28,7 @@ def test_exports_the_header(lib):
     text = open(os.path.join(INCLUDE, "moe_bandwidth_probes.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = set(re.findall(r"^int\s+(\w+)\s*\(", text, flags=re.M))
-    assert names == {"moef_probe_read", "moef_probe_copy"}
+    assert names == {"moef_probe_read", "moef_probe_copy", "moef_probe_empty"}
     for n in names:
         assert hasattr(lib, n)
     assert re.search(r"#define MOEF_PROBE_GRAIN 16384", text)
