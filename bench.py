@@ -189,7 +189,7 @@ def e4m3_steps(a, b):
 
 
 def host_threads():
-    """Host CPUs this process may run on, at most 16 (one GPU's share of a box)."""
+    """Host CPUs this process may run on, at most 16 (one GPU's share of the host)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:

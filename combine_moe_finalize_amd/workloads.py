@@ -179,6 +179,39 @@ def make_workload(T: int, H: int, E: int, top_k: int, *, rsf: float = 2.5,
                     residual=residual, gamma=gamma, eps=eps)
 
 
+def random_gather(T: int, P: int, H: int, top_k: int, *, rsf: float = 2.5, seed: int = 0,
+                  log2_mag: Optional[tuple] = None, with_residual: bool = False,
+                  name: str = "random_gather", eps: float = 1e-6) -> Workload:
+    """Inputs for grids far larger than any routed batch, drawn cheaply: P
+    real rows (no padding) and an index map of independent uniform draws
+    from [0, P), so a row may be named by many slots. Weights follow the
+    routing recipe (sigmoid of N(0,1) logits, normalised per token, fp32);
+    the residual, when asked for, is bf16(N(0,1)) and gamma bf16(U(0.5,1.5)).
+    There is no shared output."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 8])))
+    idx = rng.integers(0, P, size=(T, top_k), dtype=np.int32)
+    s = rng.standard_normal((T, top_k), dtype=np.float32)
+    np.negative(s, out=s)
+    np.exp(s, out=s)
+    s += np.float32(1.0)
+    np.reciprocal(s, out=s)                       # sigmoid
+    s /= s.sum(axis=1, keepdims=True)
+    scale = None
+    if log2_mag is not None:
+        scale = np.exp2(rng.uniform(log2_mag[0], log2_mag[1], size=P)).astype(np.float32)
+    g2 = _bf16_normal_matrix(seed, 1, P, H, scale)
+    residual = gamma = None
+    if with_residual:
+        residual = to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+        gamma = to_bf16_bits(rng.uniform(0.5, 1.5, size=H).astype(np.float32))
+    experts = np.zeros((T, top_k), np.int32)     # one expert: ids carry no layout here
+    return Workload(name=name, T=T, H=H, E=1, top_k=top_k, rsf=rsf, seed=seed,
+                    gemm2_out=g2, idx=idx, weights=s, expert_ids=experts,
+                    packed=pack_routing(experts, s), shared=None,
+                    residual=residual, gamma=gamma, eps=eps,
+                    meta={"index_map": "uniform draws from [0, P)"})
+
+
 def router_logits(T: int, E: int, seed: int, scale: float = 1.0) -> np.ndarray:
     """float32 router logits [T, E], scale * N(0,1), for the gate."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 5])))
