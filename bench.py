@@ -556,7 +556,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": counters_traffic(),
-                     "kernel": "finalize_quant_kernel<8,true>",
+                     "kernel": "finalize_quant_staged_kernel<8,true,12>",
                      "kernel_us_avg": round(avg_us, 3),
                      "kernel_us_method": f"HIP events on the launch stream around the {args.steps} "
                                          f"timed launches, divided by {args.steps}",

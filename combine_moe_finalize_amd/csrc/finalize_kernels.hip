@@ -255,6 +255,110 @@ finalize_quant_kernel(GatherArgs a, u32x2* __restrict__ out_q, uint8_t* __restri
   }
 }
 
+// ------------------------------------- UE8M0 / E4M3 quant, staged output
+
+// The same result as finalize_quant_kernel, for large grids. The quant
+// output is 5% of the launch's bytes, but written in the middle of the
+// gathers it costs about 15% of the time: the DRAM turns between reads and
+// writes all through the launch. Here every write waits until the reads are
+// done. One workgroup per CU (kStageThreads lanes) owns the CU's whole LDS
+// and processes the units u0 + b + j * gridDim.x of [u0, u1) for
+// j = 0, 1, ...: its waves take the next j from an LDS counter (so the
+// workgroup's waves finish together), keep the E4M3 codes and scale bytes of
+// unit j in LDS slot j (j < kStageUnits) or, beyond that, in one of R
+// register slots of the wave, and only after the workgroup's last gather
+// write them all. The launch start aligns the read phases of all CUs, so the
+// writes of the chip come in one burst at the end instead of being spread
+// through the reads. (A grid-wide barrier is not needed: each workgroup only
+// writes its own units.) The host sizes a launch so that every workgroup's
+// units fit: n <= kStageUnits + kStageWaves * R.
+template <int KMAX, bool EXACT, int R>
+__global__ void __launch_bounds__(kStageThreads)
+finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
+                             uint8_t* __restrict__ scale, int u0, int u1) {
+  __shared__ u32x2 stage_q[kStageUnits * kWaveLanes];
+  __shared__ uint32_t stage_e[kStageUnits];     // four scale bytes per unit
+  __shared__ int next_j;
+  constexpr int RS = R > 0 ? R : 1;
+  const int nb = (int)gridDim.x;
+  const int b = (int)blockIdx.x;
+  const int n = u1 - u0 > b ? (u1 - u0 - b + nb - 1) / nb : 0;   // this workgroup's units
+  const int nl = n < kStageUnits ? n : kStageUnits;               // of them staged in LDS
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) next_j = 0;
+  __syncthreads();
+
+  u32x2 rq[RS];            // register slots: codes, scale byte, unit index
+  uint32_t re[RS];
+  int ru[RS];
+  int cnt = 0;             // register slots in use (wave-uniform)
+  for (;;) {
+    // A wave with full register slots stops: every j left is >= nl, so it
+    // could not stage it, and the host's sizing leaves those j to the others.
+    if (R > 0 && cnt == R) break;
+    int j = 0;
+    if (lane == 0) j = atomicAdd(&next_j, 1);
+    j = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(j, 0));
+    if (j >= n) break;
+    const int unit = u0 + b + j * nb;
+    const int t = unit / a.nchunks;
+    const int colv = (unit - t * a.nchunks) * kWaveLanes + lane;
+    const bool active = colv < a.h8;
+    const int64_t col = active ? colv : a.h8 - 1;
+
+    const Side d = load_side(a, t, col, nullptr);
+    int32_t row[KMAX];
+    float w[KMAX];
+    load_route<KMAX, EXACT>(a, t, row, w);
+    float acc[8];
+    finalize_acc<KMAX, EXACT>(a, col, row, w, d, false, acc);
+
+    const u32x4 y = pack8_rne(acc);
+    const uint32_t amax = row16_max(active ? absmax8_bits(y) : 0u);
+    const int ex = ue8m0_exponent(amax);
+    const u32x2 q = e4m3x8_scaled(y, ue8m0_scale(ex));
+    if (j < nl) {
+      stage_q[j * kWaveLanes + lane] = q;
+      if ((lane & 15) == 0) reinterpret_cast<uint8_t*>(&stage_e[j])[lane >> 4] = (uint8_t)(ex + 127);
+    } else if (R > 0) {
+#pragma unroll
+      for (int s = 0; s < RS; ++s)
+        if (cnt == s) {
+          rq[s] = q;
+          re[s] = (uint32_t)(ex + 127);
+          ru[s] = unit;
+        }
+      ++cnt;
+    }
+  }
+  __syncthreads();         // every unit of the workgroup is staged
+
+#pragma unroll
+  for (int s = 0; s < RS; ++s) {
+    if (R > 0 && s < cnt) {
+      const int t = ru[s] / a.nchunks;
+      const int colv = (ru[s] - t * a.nchunks) * kWaveLanes + lane;
+      if (colv < a.h8) {
+        __builtin_nontemporal_store(rq[s], out_q + (int64_t)t * a.h8 + colv);
+        if ((lane & 15) == 0) scale[(int64_t)t * (a.h8 >> 4) + (colv >> 4)] = (uint8_t)re[s];
+      }
+    }
+  }
+  for (int x = threadIdx.x; x < nl * kWaveLanes; x += kStageThreads) {
+    const int j = x / kWaveLanes;
+    const int l = x - j * kWaveLanes;
+    const int unit = u0 + b + j * nb;
+    const int t = unit / a.nchunks;
+    const int colv = (unit - t * a.nchunks) * kWaveLanes + l;
+    if (colv < a.h8) {
+      __builtin_nontemporal_store(stage_q[x], out_q + (int64_t)t * a.h8 + colv);
+      if ((l & 15) == 0)
+        scale[(int64_t)t * (a.h8 >> 4) + (colv >> 4)] =
+            reinterpret_cast<const uint8_t*>(&stage_e[j])[l >> 4];
+    }
+  }
+}
+
 // ------------------------------------------------------------ packed decode
 
 // (expert_id << 16) | bf16(weight) -> id (logical shift) and exact fp32 weight.
@@ -405,10 +509,63 @@ hipError_t launch_finalize_rmsnorm(const Routed& r, const uint16_t* residual,
   });
 }
 
+namespace {
+
+// CUs of the current device, or 0 if the runtime cannot say.
+int device_cus() {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return ncu;
+}
+
+// The staged quant launches: as few as hold every unit (each workgroup at
+// most kStageUnits + kStageWaves * kStageRegUnits units), splitting the grid
+// into equal contiguous unit ranges; a launch whose workgroups all fit in LDS
+// takes the kernel without register slots.
+template <int KM, bool EX>
+hipError_t launch_quant_staged(const GatherArgs& a, u32x2* q, uint8_t* scale, int ncu,
+                               hipStream_t stream) {
+  const int64_t units = (int64_t)a.tokens * a.nchunks;
+  const int64_t per_launch_max = (int64_t)ncu * (kStageUnits + kStageWaves * kStageRegUnits);
+  const int64_t launches = (units + per_launch_max - 1) / per_launch_max;
+  const int64_t per_launch = (units + launches - 1) / launches;
+  for (int64_t u0 = 0; u0 < units; u0 += per_launch) {
+    const int64_t u1 = u0 + per_launch < units ? u0 + per_launch : units;
+    const int64_t per_wg = (u1 - u0 + ncu - 1) / ncu;
+    if (per_wg <= kStageUnits)
+      hipLaunchKernelGGL((finalize_quant_staged_kernel<KM, EX, 0>), dim3(ncu),
+                         dim3(kStageThreads), 0, stream, a, q, scale, (int)u0, (int)u1);
+    else
+      hipLaunchKernelGGL((finalize_quant_staged_kernel<KM, EX, kStageRegUnits>), dim3(ncu),
+                         dim3(kStageThreads), 0, stream, a, q, scale, (int)u0, (int)u1);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
 hipError_t launch_finalize_quant(const Routed& r, uint8_t* out_e4m3, uint8_t* scale_e8m0,
                                  hipStream_t stream) {
   const GatherArgs a = make_args(r);
   u32x2* q = reinterpret_cast<u32x2*>(out_e4m3);
+  const int64_t units = (int64_t)a.tokens * a.nchunks;
+  if (a.k <= kStagedMaxTopK) {
+    const int ncu = device_cus();
+    if (ncu > 0 && units >= kStagedFromUnitsPerCu * ncu) {
+      return dispatch_top_k(a.k, [&](auto km, auto ex) {
+        constexpr int KM = decltype(km)::value;
+        constexpr bool EX = decltype(ex)::value;
+        if constexpr (KM <= kStagedMaxTopK)
+          return launch_quant_staged<KM, EX>(a, q, scale_e8m0, ncu, stream);
+        else
+          return hipErrorInvalidValue;   // not reached: top_k <= 8 dispatches KM <= 8
+      });
+    }
+  }
   // Large launches reserve LDS (unused by the kernel) to hold 4 workgroups
   // per CU instead of 8: measured 1-2% faster from about a thousand tokens
   // at H = 7168 (T = 8192: 181.9-182.5 against 185.3-185.7 us), slower for a

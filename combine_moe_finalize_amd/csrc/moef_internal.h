@@ -84,6 +84,23 @@ constexpr int64_t kStreamCapFromWaves = 16384;
 constexpr size_t stream_cap_lds(int64_t waves) {
   return waves >= kStreamCapFromWaves ? lds_for_blocks_per_cu(kStreamCapBlocksPerCu) : 0;
 }
+// The UE8M0 finalize on large grids stages its output on chip and writes it
+// after the gathers (finalize_quant_staged_kernel): one workgroup of
+// kStageWaves waves per CU owns all 160 KiB of the CU's LDS, which holds the
+// codes and scale bytes of kStageUnits (token, chunk) units (516 bytes each);
+// each wave holds up to kStageRegUnits more in registers. A launch covers at
+// most (kStageUnits + kStageWaves * kStageRegUnits) units per CU; larger
+// grids take several launches. Used from kStagedFromUnitsPerCu units per CU
+// (T = 2048 at H = 7168 on 256 CUs) and top_k <= 8; below that the
+// one-wave-per-unit kernel is faster (its grid fits the chip in few rounds).
+constexpr int kStageWaves = 16;
+constexpr int kStageThreads = kStageWaves * kWaveLanes;
+constexpr int kStageUnitBytes = kChunkCols + 4;        // E4M3 codes + 4 scale bytes
+constexpr int kStageUnits = (kLdsPerCu - 256) / kStageUnitBytes;   // 317
+constexpr int kStageRegUnits = 12;
+constexpr int64_t kStagedFromUnitsPerCu = 112;
+constexpr int kStagedMaxTopK = 8;
+static_assert(kStageUnits * kStageUnitBytes + 4 <= kLdsPerCu, "staging fits the CU's LDS");
 // The RMSNorm epilogue with two column vectors per lane holds at most 20
 // waves per CU (5 per SIMD): measured faster at large T than the 24 its
 // register use would allow.
