@@ -174,3 +174,31 @@ def test_graph_capture_of_several_launches(ncu):
         torch.cuda.synchronize()
         assert torch.equal(q, q0) and torch.equal(s, s0)
     check_mirror(wl, h_u8(q0), h_u8(s0))
+
+
+def test_concurrent_calls_on_two_streams(ncu):
+    """Two staged launches in flight at once on two streams (default
+    priority): each workgroup waits on nothing outside itself, so the calls
+    share the CUs in any order and both give the single-stream bytes."""
+    H, k = 7168, 8
+    T = 2 * STAGED_FROM_UNITS_PER_CU * ncu // chunks(H)
+    wa = W.make_workload(T, H, 256, k, rsf=2.5, seed=717, log2_mag=(-8, 8))
+    wb = W.make_workload(T, H, 256, k, rsf=1.25, seed=718, log2_mag=(-8, 8))
+    ka, kb = device_inputs(wa), device_inputs(wb, packed=True)
+    announce(f"staged quant, two streams T={T} H={H}")
+    qa0, sa0 = M.moe_finalize_quant_ue8m0(**ka)
+    qb0, sb0 = M.moe_finalize_quant_ue8m0(**kb)
+    torch.cuda.synchronize()
+    qa, sa = torch.zeros_like(qa0), torch.zeros_like(sa0)
+    qb, sb = torch.zeros_like(qb0), torch.zeros_like(sb0)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            M.moe_finalize_quant_ue8m0(**ka, out_e4m3=qa, scale_e8m0=sa)
+        with torch.cuda.stream(s2):
+            M.moe_finalize_quant_ue8m0(**kb, out_e4m3=qb, scale_e8m0=sb)
+    torch.cuda.synchronize()
+    assert torch.equal(qa, qa0) and torch.equal(sa, sa0)
+    assert torch.equal(qb, qb0) and torch.equal(sb, sb0)
