@@ -91,14 +91,15 @@ constexpr size_t stream_cap_lds(int64_t waves) {
 // each wave holds up to kStageRegUnits more in registers. A launch covers at
 // most (kStageUnits + kStageWaves * kStageRegUnits) units per CU; larger
 // grids take several launches. Used from kStagedFromUnitsPerCu units per CU
-// (T = 2048 at H = 7168 on 256 CUs) and top_k <= 8; below that the
-// one-wave-per-unit kernel is faster (its grid fits the chip in few rounds).
+// (T = 1463 at H = 7168 on 256 CUs) and top_k <= 8; below that the
+// one-wave-per-unit kernel is as fast or faster (its grid fits the chip in
+// few rounds; measured equal at 70 units per CU, faster at 56).
 constexpr int kStageWaves = 16;
 constexpr int kStageThreads = kStageWaves * kWaveLanes;
 constexpr int kStageUnitBytes = kChunkCols + 4;        // E4M3 codes + 4 scale bytes
 constexpr int kStageUnits = (kLdsPerCu - 256) / kStageUnitBytes;   // 317
 constexpr int kStageRegUnits = 12;
-constexpr int64_t kStagedFromUnitsPerCu = 112;
+constexpr int64_t kStagedFromUnitsPerCu = 80;
 constexpr int kStagedMaxTopK = 8;
 static_assert(kStageUnits * kStageUnitBytes + 4 <= kLdsPerCu, "staging fits the CU's LDS");
 // The RMSNorm epilogue with two column vectors per lane holds at most 20

@@ -1,6 +1,6 @@
 """GPU parity of the UE8M0 finalize's staged-output path.
 
-From 112 (token, chunk) units per CU the quant finalize runs one workgroup per
+From 80 (token, chunk) units per CU the quant finalize runs one workgroup per
 CU that takes units from an LDS counter, keeps their codes and scale bytes in
 LDS (317 units per CU) and, past that, in 12 register slots per wave, and
 writes them after its last gather; grids larger than that take several
@@ -19,7 +19,7 @@ from gpu_helpers import DEV, announce, assert_bits_equal, device_inputs, h_u8
 
 pytestmark = pytest.mark.gpu
 
-STAGED_FROM_UNITS_PER_CU = 112
+STAGED_FROM_UNITS_PER_CU = 80
 LDS_UNITS = 317
 REG_UNITS_PER_CU = 16 * 12
 
