@@ -202,3 +202,28 @@ def test_concurrent_calls_on_two_streams(ncu):
     torch.cuda.synchronize()
     assert torch.equal(qa, qa0) and torch.equal(sa, sa0)
     assert torch.equal(qb, qb0) and torch.equal(sb, sb0)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_staged_configs(ncu, case):
+    """Seeded random shapes and options on the staged path: top_k 1..8,
+    hidden a multiple of 128 up to 4096, 80..400 units per CU (LDS slots
+    only, or LDS and register slots), fp32 or packed weights, with or without the shared output, random
+    routed scaling factor and skipped slots."""
+    rng = np.random.default_rng(4200 + case)
+    k = int(rng.integers(1, 9))
+    H = 128 * int(rng.integers(1, 33))
+    per_cu = int(rng.integers(80, 401))
+    T = -(-per_cu * ncu // chunks(H))
+    packed = bool(rng.random() < 0.5)
+    with_shared = bool(rng.random() < 0.7)
+    rsf = float(np.float32(rng.uniform(0.25, 4.0)))
+    wl = W.make_workload(T, H, 64, k, rsf=rsf, seed=int(rng.integers(1 << 30)),
+                         pad=int(rng.choice([8, 64, 128])), with_shared=with_shared,
+                         log2_mag=(-8.0, 8.0))
+    idx = wl.idx.copy()
+    idx[rng.random(idx.shape) < 0.03] = -1
+    announce(f"staged quant random case {case}: T={T} H={H} k={k} per_cu={per_cu} "
+             f"packed={packed} shared={with_shared}")
+    q, s = run_quant(wl, packed=packed, with_shared=with_shared, idx=idx)
+    check_mirror(wl, q, s, packed=packed, with_shared=with_shared, idx=idx)
