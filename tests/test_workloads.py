@@ -66,3 +66,19 @@ def test_config_shapes_and_magnitudes():
 def test_empty_token_batch():
     wl = W.make_workload(0, 128, 8, 2, seed=1)
     assert wl.idx.shape == (0, 2) and wl.P == 0 and wl.shared.shape == (0, 128)
+
+
+def test_random_gather_inputs():
+    a = W.random_gather(5000, 300, 64, 3, rsf=1.5, seed=11, with_residual=True)
+    b = W.random_gather(5000, 300, 64, 3, rsf=1.5, seed=11, with_residual=True)
+    assert np.array_equal(a.idx, b.idx) and np.array_equal(a.gemm2_out, b.gemm2_out)
+    assert a.idx.shape == (5000, 3) and a.idx.dtype == np.int32
+    assert a.idx.min() >= 0 and a.idx.max() < 300 and len(np.unique(a.idx)) == 300
+    assert a.gemm2_out.shape == (300, 64) and a.P == 300
+    assert np.all(np.abs(a.weights.astype(np.float64).sum(1) - 1) < 1e-6)
+    assert np.all(a.weights > 0) and a.weights.dtype == np.float32
+    assert a.shared is None and a.residual.shape == (5000, 64) and a.gamma.shape == (64,)
+    g = (a.gamma.astype(np.uint32) << 16).view(np.float32)
+    assert np.all((g >= 0.5) & (g <= 1.5))
+    # packed words carry the bf16 of each weight (expert id 0)
+    assert np.array_equal(a.packed.view(np.uint32) >> 16, np.zeros_like(a.idx, dtype=np.uint32))
