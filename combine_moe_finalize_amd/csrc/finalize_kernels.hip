@@ -267,11 +267,13 @@ finalize_quant_kernel(GatherArgs a, u32x2* __restrict__ out_q, uint8_t* __restri
 // workgroup's waves finish together), keep the E4M3 codes and scale bytes of
 // unit j in LDS slot j (j < kStageUnits) or, beyond that, in one of R
 // register slots of the wave, and only after the workgroup's last gather
-// write them all. The launch start aligns the read phases of all CUs, so the
-// writes of the chip come in one burst at the end instead of being spread
-// through the reads. (A grid-wide barrier is not needed: each workgroup only
-// writes its own units.) The host sizes a launch so that every workgroup's
-// units fit: n <= kStageUnits + kStageWaves * R.
+// write them all (the workgroup barrier also keeps the compiler from moving
+// any store up into the gather loop). The launch start aligns the read
+// phases of all CUs, so the chip's writes come in the last stretch of the
+// launch, while the slowest CUs finish reading, instead of all through it.
+// (No grid-wide barrier: each workgroup only writes its own units.) The host
+// sizes a launch so that every workgroup's units fit:
+// n <= kStageUnits + kStageWaves * R.
 template <int KMAX, bool EXACT, int R>
 __global__ void __launch_bounds__(kStageThreads)
 finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
