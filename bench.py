@@ -36,7 +36,8 @@ Printed: one JSON line with
              captured in a HIP graph and replayed. Kernel-only durations come
              from rocprofv3 (see profiles/),
   us_per_call  the timed operation on its first T = 1, 2, 4, ..., 8192
-             tokens, the decode finalize at T = 1..256, and an empty kernel
+             tokens, the plain bf16 finalize of the same tokens at
+             T = 256..8192, the decode finalize at T = 1..256, and an empty kernel
              (one wave, no memory access), all per call under HIP-graph
              replay: the empty kernel is the floor under any call's time.
 """
@@ -576,7 +577,7 @@ def main():
             "headline_frac_of_copy": round(achieved / copy_gbs, 4)}
     # us/call of the same operation on the first T tokens of the same workload,
     # T = 1, 2, 4, ..., 8192, per call under HIP-graph replay
-    curve = {}
+    curve, curve_plain = {}, {}
     if not args.no_sweep:
         idx_all, w_all, sh_all = (kw["expanded_idx_to_permuted_idx"], kw["topk_weights"],
                                   kw["shared_out"])
@@ -593,6 +594,21 @@ def main():
                               "frac": round(gbs / HBM_PEAK_GBS, 4)}
             log(f"prefill op T={Tc}: {us:.3f} us/call, {gbs:.0f} GB/s")
             Tc *= 2
+        # the plain bf16 finalize of the same tokens (no quant epilogue)
+        out_bf16 = torch.empty((T, H), dtype=torch.bfloat16, device="cuda:0")
+        for Tc in (256, 1024, 2048, 4096, 8192):
+            if Tc > T:
+                break
+            kc = dict(kw, expanded_idx_to_permuted_idx=idx_all[:Tc], topk_weights=w_all[:Tc],
+                      shared_out=sh_all[:Tc])
+            oc = out_bf16[:Tc]
+            us = graph_us(torch, lambda: M.moe_finalize(**kc, out=oc),
+                          n=20 if Tc <= 256 else 5, reps=5 if Tc <= 1024 else 2)
+            gbs = bytes_plain(Tc, H, k) / us / 1e3
+            curve_plain[str(Tc)] = {"us": round(us, 3), "gbs": round(gbs, 1),
+                                    "frac": round(gbs / HBM_PEAK_GBS, 4)}
+            log(f"plain finalize T={Tc}: {us:.3f} us/call, {gbs:.0f} GB/s")
+        del out_bf16
         step()                                   # the timed launches' outputs again
         torch.cuda.synchronize()
     # the timed launches' outputs, kept on the host for the CPU leg's parity report
@@ -608,6 +624,7 @@ def main():
                     if r["case"] == "decode"}
         result["us_per_call"] = {
             "finalize_quant_ue8m0_H7168_k8_graph_replay": curve,
+            "finalize_bf16_H7168_k8_graph_replay": curve_plain,
             "finalize_H4096_k8_graph_replay": per_call,
             "empty_kernel_graph_replay": round(launch_floor_us(torch), 3)}
     if not args.no_cpu_baseline:

@@ -361,6 +361,82 @@ finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
   }
 }
 
+// ---------------------------------------------- plain finalize, staged output
+
+// finalize_kernel's result through the staging scheme of
+// finalize_quant_staged_kernel above (one workgroup per CU, units
+// u0 + b + j * gridDim.x taken from an LDS counter, writes after the
+// workgroup's last gather). A unit's output is its 1 KiB of bf16: LDS holds
+// kStagePlainUnits of them, each wave R more in registers. The output is 10%
+// of the plain finalize's bytes (k = 8), so keeping it out of the read phase
+// gains more than for the quant output.
+template <int KMAX, bool EXACT, int R>
+__global__ void __launch_bounds__(kStageThreads)
+finalize_staged_kernel(GatherArgs a, u32x4* __restrict__ out, int u0, int u1) {
+  __shared__ u32x4 stage_o[kStagePlainUnits * kWaveLanes];
+  __shared__ int next_j;
+  constexpr int RS = R > 0 ? R : 1;
+  const int nb = (int)gridDim.x;
+  const int b = (int)blockIdx.x;
+  const int n = u1 - u0 > b ? (u1 - u0 - b + nb - 1) / nb : 0;       // this workgroup's units
+  const int nl = n < kStagePlainUnits ? n : kStagePlainUnits;         // of them staged in LDS
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) next_j = 0;
+  __syncthreads();
+
+  u32x4 ro[RS];            // register slots: bf16 output vector, unit index
+  int ru[RS];
+  int cnt = 0;             // register slots in use (wave-uniform)
+  for (;;) {
+    if (R > 0 && cnt == R) break;   // every j left is >= nl (see the quant kernel)
+    int j = 0;
+    if (lane == 0) j = atomicAdd(&next_j, 1);
+    j = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(j, 0));
+    if (j >= n) break;
+    const int unit = u0 + b + j * nb;
+    const int t = unit / a.nchunks;
+    const int colv = (unit - t * a.nchunks) * kWaveLanes + lane;
+    const int64_t col = colv < a.h8 ? colv : a.h8 - 1;
+
+    const Side d = load_side(a, t, col, nullptr);
+    int32_t row[KMAX];
+    float w[KMAX];
+    load_route<KMAX, EXACT>(a, t, row, w);
+    float acc[8];
+    finalize_acc<KMAX, EXACT>(a, col, row, w, d, false, acc);
+    const u32x4 y = pack8_rne(acc);
+    if (j < nl) {
+      stage_o[j * kWaveLanes + lane] = y;
+    } else if (R > 0) {
+#pragma unroll
+      for (int s = 0; s < RS; ++s)
+        if (cnt == s) {
+          ro[s] = y;
+          ru[s] = unit;
+        }
+      ++cnt;
+    }
+  }
+  __syncthreads();         // every unit of the workgroup is staged
+
+#pragma unroll
+  for (int s = 0; s < RS; ++s) {
+    if (R > 0 && s < cnt) {
+      const int t = ru[s] / a.nchunks;
+      const int colv = (ru[s] - t * a.nchunks) * kWaveLanes + lane;
+      if (colv < a.h8) __builtin_nontemporal_store(ro[s], out + (int64_t)t * a.h8 + colv);
+    }
+  }
+  for (int x = threadIdx.x; x < nl * kWaveLanes; x += kStageThreads) {
+    const int j = x / kWaveLanes;
+    const int l = x - j * kWaveLanes;
+    const int unit = u0 + b + j * nb;
+    const int t = unit / a.nchunks;
+    const int colv = (unit - t * a.nchunks) * kWaveLanes + l;
+    if (colv < a.h8) __builtin_nontemporal_store(stage_o[x], out + (int64_t)t * a.h8 + colv);
+  }
+}
+
 // ------------------------------------------------------------ packed decode
 
 // (expert_id << 16) | bf16(weight) -> id (logical shift) and exact fp32 weight.
@@ -463,9 +539,84 @@ unsigned int plain_blocks(const GatherArgs& a) {
 
 }  // namespace
 
+namespace {
+
+// CUs of the current device, or 0 if the runtime cannot say.
+int device_cus() {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return ncu;
+}
+
+// Splits the grid's units into as few launches as hold every unit (a launch
+// covers at most ncu * (lds_units + kStageWaves * reg_units) of them), in
+// equal contiguous ranges, and calls launch(u0, u1, registers) for each;
+// `registers` says whether a workgroup's units can exceed lds_units (it then
+// needs the kernel with register slots).
+template <typename F>
+hipError_t staged_launches(const GatherArgs& a, int ncu, int lds_units, int reg_units,
+                           F&& launch) {
+  const int64_t units = (int64_t)a.tokens * a.nchunks;
+  const int64_t per_launch_max = (int64_t)ncu * (lds_units + kStageWaves * reg_units);
+  const int64_t launches = (units + per_launch_max - 1) / per_launch_max;
+  const int64_t per_launch = (units + launches - 1) / launches;
+  for (int64_t u0 = 0; u0 < units; u0 += per_launch) {
+    const int64_t u1 = u0 + per_launch < units ? u0 + per_launch : units;
+    const int64_t per_wg = (u1 - u0 + ncu - 1) / ncu;
+    launch((int)u0, (int)u1, per_wg > lds_units);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int KM, bool EX>
+hipError_t launch_quant_staged(const GatherArgs& a, u32x2* q, uint8_t* scale, int ncu,
+                               hipStream_t stream) {
+  return staged_launches(a, ncu, kStageUnits, kStageRegUnits, [&](int u0, int u1, bool regs) {
+    if (regs)
+      hipLaunchKernelGGL((finalize_quant_staged_kernel<KM, EX, kStageRegUnits>), dim3(ncu),
+                         dim3(kStageThreads), 0, stream, a, q, scale, u0, u1);
+    else
+      hipLaunchKernelGGL((finalize_quant_staged_kernel<KM, EX, 0>), dim3(ncu),
+                         dim3(kStageThreads), 0, stream, a, q, scale, u0, u1);
+  });
+}
+
+template <int KM, bool EX>
+hipError_t launch_plain_staged(const GatherArgs& a, u32x4* o, int ncu, hipStream_t stream) {
+  return staged_launches(a, ncu, kStagePlainUnits, kStagePlainRegUnits,
+                         [&](int u0, int u1, bool regs) {
+    if (regs)
+      hipLaunchKernelGGL((finalize_staged_kernel<KM, EX, kStagePlainRegUnits>), dim3(ncu),
+                         dim3(kStageThreads), 0, stream, a, o, u0, u1);
+    else
+      hipLaunchKernelGGL((finalize_staged_kernel<KM, EX, 0>), dim3(ncu),
+                         dim3(kStageThreads), 0, stream, a, o, u0, u1);
+  });
+}
+
+}  // namespace
+
 hipError_t launch_finalize(const Routed& r, uint16_t* out, hipStream_t stream) {
   const GatherArgs a = make_args(r);
   u32x4* o = reinterpret_cast<u32x4*>(out);
+  const int64_t units = (int64_t)a.tokens * a.nchunks;
+  if (a.k <= kStagedMaxTopK) {
+    const int ncu = device_cus();
+    if (ncu > 0 && units >= kStagedPlainFromUnitsPerCu * ncu) {
+      return dispatch_top_k(a.k, [&](auto km, auto ex) {
+        constexpr int KM = decltype(km)::value;
+        constexpr bool EX = decltype(ex)::value;
+        if constexpr (KM <= kStagedMaxTopK)
+          return launch_plain_staged<KM, EX>(a, o, ncu, stream);
+        else
+          return hipErrorInvalidValue;   // not reached: top_k <= 8 dispatches KM <= 8
+      });
+    }
+  }
   const size_t lds = stream_cap_lds((int64_t)a.tokens * a.nchunks);
   return dispatch_top_k(a.k, [&](auto km, auto ex) {
     constexpr int KM = decltype(km)::value;
@@ -511,44 +662,6 @@ hipError_t launch_finalize_rmsnorm(const Routed& r, const uint16_t* residual,
   });
 }
 
-namespace {
-
-// CUs of the current device, or 0 if the runtime cannot say.
-int device_cus() {
-  int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  return ncu;
-}
-
-// The staged quant launches: as few as hold every unit (each workgroup at
-// most kStageUnits + kStageWaves * kStageRegUnits units), splitting the grid
-// into equal contiguous unit ranges; a launch whose workgroups all fit in LDS
-// takes the kernel without register slots.
-template <int KM, bool EX>
-hipError_t launch_quant_staged(const GatherArgs& a, u32x2* q, uint8_t* scale, int ncu,
-                               hipStream_t stream) {
-  const int64_t units = (int64_t)a.tokens * a.nchunks;
-  const int64_t per_launch_max = (int64_t)ncu * (kStageUnits + kStageWaves * kStageRegUnits);
-  const int64_t launches = (units + per_launch_max - 1) / per_launch_max;
-  const int64_t per_launch = (units + launches - 1) / launches;
-  for (int64_t u0 = 0; u0 < units; u0 += per_launch) {
-    const int64_t u1 = u0 + per_launch < units ? u0 + per_launch : units;
-    const int64_t per_wg = (u1 - u0 + ncu - 1) / ncu;
-    if (per_wg <= kStageUnits)
-      hipLaunchKernelGGL((finalize_quant_staged_kernel<KM, EX, 0>), dim3(ncu),
-                         dim3(kStageThreads), 0, stream, a, q, scale, (int)u0, (int)u1);
-    else
-      hipLaunchKernelGGL((finalize_quant_staged_kernel<KM, EX, kStageRegUnits>), dim3(ncu),
-                         dim3(kStageThreads), 0, stream, a, q, scale, (int)u0, (int)u1);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
-}  // namespace
 
 hipError_t launch_finalize_quant(const Routed& r, uint8_t* out_e4m3, uint8_t* scale_e8m0,
                                  hipStream_t stream) {

@@ -102,6 +102,14 @@ constexpr int kStageRegUnits = 12;
 constexpr int64_t kStagedFromUnitsPerCu = 80;
 constexpr int kStagedMaxTopK = 8;
 static_assert(kStageUnits * kStageUnitBytes + 4 <= kLdsPerCu, "staging fits the CU's LDS");
+// The plain finalize stages the same way: 1 KiB of bf16 output per unit, 159
+// units in LDS and up to 8 more per wave in registers (four VGPRs each); used
+// from 48 units per CU (T = 878 at H = 7168 on 256 CUs), top_k <= 8.
+constexpr int kStagePlainUnitBytes = kChunkCols * 2;
+constexpr int kStagePlainUnits = (kLdsPerCu - 256) / kStagePlainUnitBytes;   // 159
+constexpr int kStagePlainRegUnits = 8;
+constexpr int64_t kStagedPlainFromUnitsPerCu = 48;
+static_assert(kStagePlainUnits * kStagePlainUnitBytes + 4 <= kLdsPerCu, "staging fits the LDS");
 // The RMSNorm epilogue with two column vectors per lane holds at most 20
 // waves per CU (5 per SIMD): measured faster at large T than the 24 its
 // register use would allow.
