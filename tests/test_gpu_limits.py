@@ -11,6 +11,7 @@
   bit with the oracle's fp32 mirror (normed within 2e-2, relative).
 * The most partials one expert-parallel combine may sum
   (MOEF_MAX_EP_PARTIALS).
+* The staged-output plain and UE8M0 finalize at the largest hidden size.
 """
 import os
 import re
@@ -192,3 +193,23 @@ def test_ep_combine_at_maximum_partials():
     out = M.moe_finalize_ep_combine(d_bf16(p), shared_out=d_bf16(sh))
     torch.cuda.synchronize()
     assert_bits_equal(h_bits(out), O.ep_combine_mirror(p, sh), "combine of the most partials")
+
+
+def test_staged_paths_at_maximum_hidden():
+    """10 tokens of the largest hidden size: 20 480 units, so both the plain
+    and the UE8M0 finalize take their staged-output kernels on 256 CUs."""
+    H = LIM["MOEF_MAX_HIDDEN"]
+    wl = W.make_workload(10, H, 4, 2, rsf=2.5, seed=907, pad=8, log2_mag=(-8, 8))
+    announce(f"staged finalize + quant at H={H} T=10 k=2")
+    kw = device_inputs(wl)
+    out = M.moe_finalize(**kw)
+    q, s = M.moe_finalize_quant_ue8m0(**kw)
+    torch.cuda.synchronize()
+    got, q, s = h_bits(out), h_u8(q), h_u8(s)
+    del kw, out
+    mirror, _ = O.finalize_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
+                                  shared=wl.shared, rsf=wl.rsf)
+    assert_bits_equal(got, mirror, "finalize vs fp32 mirror")
+    mq, ms, _ = O.quant_ue8m0(mirror)
+    assert_bits_equal(s, ms, "UE8M0 scales")
+    assert_bits_equal(q, mq, "E4M3 codes")
