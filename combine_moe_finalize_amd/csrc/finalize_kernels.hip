@@ -272,8 +272,9 @@ finalize_quant_kernel(GatherArgs a, u32x2* __restrict__ out_q, uint8_t* __restri
 // phases of all CUs, so the chip's writes come in the last stretch of the
 // launch, while the slowest CUs finish reading, instead of all through it.
 // (No grid-wide barrier: each workgroup only writes its own units.) The host
-// sizes a launch so that every workgroup's units fit:
-// n <= kStageUnits + kStageWaves * R.
+// sizes a launch so that every workgroup's units fit,
+// n <= kStageUnits + kStageWaves * R; a unit that still found no slot would
+// be written at once, so no sizing can drop one.
 template <int KMAX, bool EXACT, int R>
 __global__ void __launch_bounds__(kStageThreads)
 finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
@@ -295,9 +296,6 @@ finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
   int ru[RS];
   int cnt = 0;             // register slots in use (wave-uniform)
   for (;;) {
-    // A wave with full register slots stops: every j left is >= nl, so it
-    // could not stage it, and the host's sizing leaves those j to the others.
-    if (R > 0 && cnt == R) break;
     int j = 0;
     if (lane == 0) j = atomicAdd(&next_j, 1);
     j = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(j, 0));
@@ -322,7 +320,7 @@ finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
     if (j < nl) {
       stage_q[j * kWaveLanes + lane] = q;
       if ((lane & 15) == 0) reinterpret_cast<uint8_t*>(&stage_e[j])[lane >> 4] = (uint8_t)(ex + 127);
-    } else if (R > 0) {
+    } else if (R > 0 && cnt < R) {
 #pragma unroll
       for (int s = 0; s < RS; ++s)
         if (cnt == s) {
@@ -331,9 +329,15 @@ finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
           ru[s] = unit;
         }
       ++cnt;
+    } else if (active) {
+      // No slot left (the host sizes launches so that this is not reached):
+      // write now, as the one-wave-per-unit kernel does, so that no unit is
+      // ever dropped whatever the sizing.
+      __builtin_nontemporal_store(q, out_q + (int64_t)t * a.h8 + colv);
+      if ((lane & 15) == 0) scale[(int64_t)t * (a.h8 >> 4) + (colv >> 4)] = (uint8_t)(ex + 127);
     }
   }
-  __syncthreads();         // every unit of the workgroup is staged
+  __syncthreads();         // every unit of the workgroup is staged or written
 
 #pragma unroll
   for (int s = 0; s < RS; ++s) {
@@ -388,7 +392,6 @@ finalize_staged_kernel(GatherArgs a, u32x4* __restrict__ out, int u0, int u1) {
   int ru[RS];
   int cnt = 0;             // register slots in use (wave-uniform)
   for (;;) {
-    if (R > 0 && cnt == R) break;   // every j left is >= nl (see the quant kernel)
     int j = 0;
     if (lane == 0) j = atomicAdd(&next_j, 1);
     j = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(j, 0));
@@ -407,7 +410,7 @@ finalize_staged_kernel(GatherArgs a, u32x4* __restrict__ out, int u0, int u1) {
     const u32x4 y = pack8_rne(acc);
     if (j < nl) {
       stage_o[j * kWaveLanes + lane] = y;
-    } else if (R > 0) {
+    } else if (R > 0 && cnt < R) {
 #pragma unroll
       for (int s = 0; s < RS; ++s)
         if (cnt == s) {
@@ -415,9 +418,11 @@ finalize_staged_kernel(GatherArgs a, u32x4* __restrict__ out, int u0, int u1) {
           ru[s] = unit;
         }
       ++cnt;
+    } else if (colv < a.h8) {
+      __builtin_nontemporal_store(y, out + (int64_t)t * a.h8 + colv);   // no slot left
     }
   }
-  __syncthreads();         // every unit of the workgroup is staged
+  __syncthreads();         // every unit of the workgroup is staged or written
 
 #pragma unroll
   for (int s = 0; s < RS; ++s) {
