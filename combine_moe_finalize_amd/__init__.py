@@ -8,12 +8,16 @@ library in-tree.
 from ._binding import (  # noqa: F401
     DEVERR_INDEX_OUT_OF_RANGE,
     MoeFinalizeError,
+    OP_FINALIZE,
+    OP_QUANT_UE8M0,
+    OP_RESIDUAL_RMSNORM,
     abi_version,
     load_library,
     moe_act_quant_fp8_amax,
     moe_act_quant_fp8_ue8m0,
     moe_allreduce_residual_rmsnorm,
     moe_finalize,
+    moe_finalize_describe_launch,
     moe_finalize_ep_combine,
     moe_finalize_quant_ue8m0,
     moe_finalize_residual_rmsnorm,

@@ -35,6 +35,7 @@ c_f32 = ctypes.c_float
 
 MOEF_OK = 0
 QUANT_BLOCK = 128
+OP_FINALIZE, OP_RESIDUAL_RMSNORM, OP_QUANT_UE8M0 = 0, 1, 2
 DEVERR_INDEX_OUT_OF_RANGE = 1
 
 _ROUTED = [c_void_p, c_i64, c_void_p, c_void_p, c_void_p, c_void_p, c_f32]
@@ -52,6 +53,8 @@ _SIGNATURES = {
     "moe_act_quant_fp8_amax": [c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_void_p],
     "moe_allreduce_residual_rmsnorm": [ctypes.POINTER(c_void_p), c_i32, c_void_p, c_void_p, c_f32,
                                        c_void_p, c_void_p, c_i64, c_i64, c_void_p],
+    "moe_finalize_describe_launch": [c_i32, c_i64, c_i64, c_i32, c_void_p, ctypes.c_char_p,
+                                     c_i64],
     "moe_finalize_status_string": [ctypes.c_int],
     "moe_finalize_abi_version": [],
 }
@@ -89,6 +92,21 @@ def status_string(status: int) -> str:
 
 def abi_version() -> int:
     return load_library().moe_finalize_abi_version()
+
+
+def moe_finalize_describe_launch(op: int, num_tokens: int, hidden: int, top_k: int,
+                                 device=None) -> str:
+    """The kernel (as profilers print it), launch count and grid that a call
+    of this shape runs on `device` (default: the current one)."""
+    if device is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    buf = ctypes.create_string_buffer(256)
+    st = load_library().moe_finalize_describe_launch(int(op), int(num_tokens), int(hidden),
+                                                     int(top_k), _stream(torch.device(device)),
+                                                     buf, len(buf))
+    if st != MOEF_OK:
+        raise MoeFinalizeError("moe_finalize_describe_launch", st)
+    return buf.value.decode()
 
 
 # ------------------------------------------------------------- marshalling

@@ -67,6 +67,38 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// ------------------------------------------------ kernel argument loads
+
+// Makes the compiler load a kernel argument no later than this point: left
+// alone, it defers the load of an output pointer (or of a scalar used after a
+// barrier) to its use, which puts one more dependent memory round trip at
+// the end of a short kernel. The empty asm reads the value in scalar
+// registers; it counts as a memory access, so callers place it after their
+// last load (a load after it could no longer be a scalar load).
+template <typename T>
+__device__ __forceinline__ void load_now(T v) {
+  asm volatile("" ::"s"(v));
+}
+
+// ------------------------------------------------ workgroup work counter
+
+// The next unit of the calling wave from a workgroup's LDS counter (which
+// starts at 0): lane 0 adds one and the old value is broadcast, so the
+// result is wave-uniform. A loop around this fetch must not end its body
+// with a store made by lane 0 alone: the optimizer can then send lanes
+// 1..63 from that store straight back to the broadcast, which the compiled
+// code turns into an inner loop they only leave once lane 0's (stale) value
+// reaches the loop bound, and the wave never finishes. Callers bound their
+// loop by the unit count and stop on any value outside [0, n).
+// (ds_append would fetch without a lane-0 branch, but it takes the counter's
+// address from the low 16 bits of M0, so it cannot reach a counter placed
+// after 64 KiB of staging arrays.)
+__device__ __forceinline__ int next_unit(int* counter) {
+  int j = 0;
+  if ((threadIdx.x & 63) == 0) j = atomicAdd(counter, 1);
+  return __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(j, 0));
+}
+
 // ---------------------------------------------------- RMSNorm of one row
 // One workgroup holds one row; lane t of it owns the 16-byte column vectors
 // t + i * blockDim.x, i < CPT, so wave w's vector i is 512-column chunk

@@ -39,6 +39,8 @@
 //    ("[FP8][MoE] Honor UE8M0 activation scales in Triton MoE", Motivation
 //    and "More context".)
 
+#include <atomic>
+
 #include "device_common.h"
 #include "moef_internal.h"
 
@@ -68,31 +70,63 @@ struct GatherArgs {
 
 // ------------------------------------------------------------- gather core
 
-// Loads the token's routing: gathered row (or -1 when the slot is skipped)
-// and w' = fp32(w * rsf). Reads are wave-uniform (scalar loads).
+// A call's latency at decode sizes is a chain of dependent round trips, so
+// the helpers below are called in an order that keeps it short: the
+// routing-independent operands (shared, residual) first, then the token's
+// row indices, then the row loads they address, and only then the weights,
+// which the compiler can fetch while the rows are in flight. Nothing
+// branches between the index load and the row loads (an out-of-range index
+// is reported after the store, by report_out_of_range).
+
+// The token's gathered rows, or -1 where a slot is skipped: an index < 0
+// names an expert that is not local, one >= num_rows is out of range (the
+// return value says whether one was). Wave-uniform scalar loads.
 template <int KMAX, bool EXACT>
-__device__ __forceinline__ void load_route(const GatherArgs& a, int t,
-                                           int32_t row[KMAX], float w[KMAX]) {
+__device__ __forceinline__ bool load_rows(const GatherArgs& a, int t, int32_t row[KMAX]) {
   const int64_t base = (int64_t)t * a.k;
-  uint32_t word[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     row[j] = -1;
-    word[j] = 0u;
-    if (EXACT || j < a.k) {
-      row[j] = a.idx[base + j];
-      word[j] = a.w[base + j];
-    }
+    if (EXACT || j < a.k) row[j] = a.idx[base + j];
   }
   bool oob = false;
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    w[j] = __uint_as_float(a.packed ? (word[j] << 16) : word[j]) * a.rsf;
-    if (row[j] >= a.num_rows) {            // out of range: skip and report
-      oob = true;
-      row[j] = -1;
-    }                                      // negative: expert not local, skip
+    oob = oob || row[j] >= a.num_rows;
+    row[j] = row[j] >= a.num_rows ? -1 : row[j];
   }
+  return oob;
+}
+
+// The 16-byte vectors of the token's rows at column vector col, every load
+// issued before any is used.
+template <int KMAX, bool EXACT>
+__device__ __forceinline__ void load_gathers(const GatherArgs& a, int64_t col,
+                                             const int32_t row[KMAX], u32x4 v[KMAX]) {
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    v[j] = u32x4{0u, 0u, 0u, 0u};
+    if ((EXACT || j < a.k) && row[j] >= 0)
+      v[j] = __builtin_nontemporal_load(a.g2 + (int64_t)row[j] * a.h8 + col);
+  }
+}
+
+// w' = fp32(w * rsf) per slot, from fp32 weights or the bf16 half of packed
+// words, kept in registers. Wave-uniform scalar loads.
+template <int KMAX, bool EXACT>
+__device__ __forceinline__ void load_weights(const GatherArgs& a, int t, float w[KMAX]) {
+  const int64_t base = (int64_t)t * a.k;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    uint32_t word = 0u;
+    if (EXACT || j < a.k) word = a.w[base + j];
+    w[j] = __uint_as_float(a.packed ? (word << 16) : word) * a.rsf;
+  }
+}
+
+// Sets the caller's error flag if any slot of the wave's token was out of
+// range (after the wave's stores, off the call's critical path).
+__device__ __forceinline__ void report_out_of_range(const GatherArgs& a, bool oob) {
   if (oob && a.err != nullptr && (threadIdx.x & 63) == 0)
     atomicOr(a.err, MOEF_DEVERR_INDEX_OUT_OF_RANGE);
 }
@@ -116,17 +150,12 @@ __device__ __forceinline__ Side load_side(const GatherArgs& a, int t, int64_t co
 }
 
 // acc[0..7] for columns [8*col, 8*col + 8): the weighted sum of the gathered
-// rows, then + shared, then + residual (when given), each step in fp32.
+// rows in slot order, then + shared, then + residual (when given), each step
+// in fp32.
 template <int KMAX, bool EXACT>
-__device__ __forceinline__ void finalize_acc(const GatherArgs& a, int64_t col,
-                                             const int32_t row[KMAX], const float w[KMAX],
-                                             const Side& d, bool has_residual, float acc[8]) {
-  u32x4 v[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if ((EXACT || j < a.k) && row[j] >= 0)
-      v[j] = __builtin_nontemporal_load(a.g2 + (int64_t)row[j] * a.h8 + col);
-  }
+__device__ __forceinline__ void reduce_rows(const GatherArgs& a, const int32_t row[KMAX],
+                                            const u32x4 v[KMAX], const float w[KMAX],
+                                            const Side& d, bool has_residual, float acc[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 #pragma unroll
@@ -152,6 +181,37 @@ __device__ __forceinline__ void finalize_acc(const GatherArgs& a, int64_t col,
   }
 }
 
+// One column vector's gather in flight: the token's rows, their loaded
+// vectors, the weights, and whether a slot was out of range.
+template <int KMAX>
+struct Gathered {
+  int32_t row[KMAX];
+  u32x4 v[KMAX];
+  float w[KMAX];
+  bool oob;
+};
+
+// Issues the loads of one column vector of token t: row indices, then the
+// row loads, then the weights (the order above).
+template <int KMAX, bool EXACT>
+__device__ __forceinline__ void issue_gather(const GatherArgs& a, int t, int64_t col,
+                                             Gathered<KMAX>& g) {
+  g.oob = load_rows<KMAX, EXACT>(a, t, g.row);
+  load_gathers<KMAX, EXACT>(a, col, g.row, g.v);
+  load_weights<KMAX, EXACT>(a, t, g.w);
+}
+
+// The finalize of one column vector of token t. Returns whether a slot was
+// out of range.
+template <int KMAX, bool EXACT>
+__device__ __forceinline__ bool finalize_vector(const GatherArgs& a, int t, int64_t col,
+                                                const Side& d, bool has_residual, float acc[8]) {
+  Gathered<KMAX> g;
+  issue_gather<KMAX, EXACT>(a, t, col, g);
+  reduce_rows<KMAX, EXACT>(a, g.row, g.v, g.w, d, has_residual, acc);
+  return g.oob;
+}
+
 // ------------------------------------------------------------------ plain
 
 template <int KMAX, bool EXACT>
@@ -159,21 +219,28 @@ __global__ void __launch_bounds__(kWavesPerBlock * kWaveLanes)
 finalize_kernel(GatherArgs a, u32x4* __restrict__ out) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  const int unit = (int)blockIdx.x * kWavesPerBlock + wave;
-  if ((int64_t)unit >= (int64_t)a.tokens * a.nchunks) return;   // whole waves
+  // Waves past the last unit (the grid's last workgroup) redo the last unit
+  // and store nothing, instead of returning early: no branch then stands
+  // between the kernel's first argument loads and the rest of them.
+  const int units = a.tokens * a.nchunks;
+  const bool live = (int)blockIdx.x * kWavesPerBlock + wave < units;
+  const int unit = live ? (int)blockIdx.x * kWavesPerBlock + wave : units - 1;
   const int t = unit / a.nchunks;
   const int colv = (unit - t * a.nchunks) * kWaveLanes + lane;
   const bool active = colv < a.h8;
   const int64_t col = active ? colv : a.h8 - 1;   // keep every lane's loads in bounds
 
   const Side d = load_side(a, t, col, nullptr);
-  int32_t row[KMAX];
-  float w[KMAX];
-  load_route<KMAX, EXACT>(a, t, row, w);
+  Gathered<KMAX> g;
+  issue_gather<KMAX, EXACT>(a, t, col, g);
+  load_now(out);           // after every load: the asm counts as a memory access
+  load_now(a.err);
   float acc[8];
-  finalize_acc<KMAX, EXACT>(a, col, row, w, d, false, acc);
+  reduce_rows<KMAX, EXACT>(a, g.row, g.v, g.w, d, false, acc);
+  const bool oob = g.oob;
 
-  if (active) __builtin_nontemporal_store(pack8_rne(acc), out + (int64_t)t * a.h8 + colv);
+  if (live && active) __builtin_nontemporal_store(pack8_rne(acc), out + (int64_t)t * a.h8 + colv);
+  report_out_of_range(a, oob);
 }
 
 // ------------------------------------------------------- residual + RMSNorm
@@ -199,8 +266,8 @@ finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __rest
     gv[i] = gamma[col];
   }
   int32_t row[KMAX];
+  const bool oob = load_rows<KMAX, EXACT>(a, t, row);
   float w[KMAX];
-  load_route<KMAX, EXACT>(a, t, row, w);
 
   float ro[CPT][8];
 #pragma unroll
@@ -208,8 +275,19 @@ finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __rest
     const int colv = threadIdx.x + i * nthreads;
     const bool active = colv < a.h8;
     const int64_t col = active ? colv : a.h8 - 1;
+    u32x4 v[KMAX];
+    load_gathers<KMAX, EXACT>(a, col, row, v);
+    if (i == 0) {
+      load_weights<KMAX, EXACT>(a, t, w);
+      load_now(residual_out);  // after the loads: the asm counts as a memory access
+      load_now(normed);
+      load_now(eps);
+      load_now(inv_hidden);
+      load_now(a.err);
+      load_now((int)blockDim.x);
+    }
     float acc[8];
-    finalize_acc<KMAX, EXACT>(a, col, row, w, d[i], true, acc);
+    reduce_rows<KMAX, EXACT>(a, row, v, w, d[i], true, acc);
     const u32x4 rb = pack8_rne(acc);
     unpack8(rb, ro[i]);                     // the stored bf16 residual_out
     float ss = 0.0f;
@@ -222,6 +300,95 @@ finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __rest
   }
   const float inv = row_inv_rms<CPT>(partial, inv_hidden, eps);
   store_normed<CPT>(ro, gv, inv, a.h8, normed + (int64_t)t * a.h8);
+  report_out_of_range(a, oob);
+}
+
+// ------------------------------------- residual + RMSNorm, staged output
+
+// finalize_rmsnorm_kernel's result for large grids, with every write after
+// the workgroup's gathers (the scheme of finalize_quant_staged_kernel below).
+// One workgroup per CU owns whole tokens t0 + b + i * gridDim.x, i < ntok,
+// and its waves take the (token, chunk) units j = i * nchunks + c from the
+// LDS counter. Unit j leaves its residual_out vector (1 KiB of bf16) in LDS
+// slot j and its sum of squares, reduced over the wave exactly as the
+// one-workgroup-per-token kernel reduces a chunk, in sumsq[j]. After the
+// last gather each token's 1 / rms is formed from its chunk sums added in
+// chunk order, as row_inv_rms does, so the two kernels give bit-identical
+// results; then the workgroup writes residual_out and normed. A token's
+// residual is read only by the workgroup that writes its residual_out, and
+// before it does, so residual_out may alias residual. The host sizes
+// launches so that ntok * nchunks <= kStageRmsUnits.
+template <int KMAX, bool EXACT>
+__global__ void __launch_bounds__(kStageThreads)
+finalize_rmsnorm_staged_kernel(GatherArgs a, const u32x4* residual,
+                               const u32x4* __restrict__ gamma, float eps, float inv_hidden,
+                               u32x4* residual_out, u32x4* __restrict__ normed, int t0, int t1) {
+  __shared__ u32x4 stage_r[kStageRmsUnits * kWaveLanes];
+  __shared__ float sumsq[kStageRmsUnits];
+  __shared__ float inv_rms[kStageRmsUnits];     // per token
+  __shared__ int next_j;
+  const int nb = (int)gridDim.x;
+  const int b = (int)blockIdx.x;
+  const int nch = a.nchunks;
+  int ntok = t1 - t0 > b ? (t1 - t0 - b + nb - 1) / nb : 0;
+  if (ntok > kStageRmsUnits / nch) ntok = kStageRmsUnits / nch;   // launches are sized below it
+  const int n = ntok * nch;
+  const int lane = threadIdx.x & 63;
+  bool oob = false;
+  if (threadIdx.x == 0) next_j = 0;
+  __syncthreads();
+
+  for (int it = 0; it < n; ++it) {
+    const int j = next_unit(&next_j);
+    if ((unsigned)j >= (unsigned)n) break;
+    const int i = j / nch;
+    const int t = t0 + b + i * nb;
+    const int colv = (j - i * nch) * kWaveLanes + lane;
+    const bool active = colv < a.h8;
+    const int64_t col = active ? colv : a.h8 - 1;
+
+    const Side d = load_side(a, t, col, residual + (int64_t)t * a.h8);
+    float acc[8];
+    oob = finalize_vector<KMAX, EXACT>(a, t, col, d, true, acc) || oob;
+    const u32x4 rb = pack8_rne(acc);
+    float ro[8];
+    unpack8(rb, ro);
+    float ss = 0.0f;
+    if (active) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = ss + ro[e] * ro[e];
+    }
+    const float chunk_sum = wave_sum(ss);
+    stage_r[j * kWaveLanes + lane] = rb;
+    sumsq[j] = chunk_sum;                   // every lane stores the same value
+  }
+  __syncthreads();         // every unit of the workgroup is staged
+
+  for (int i = threadIdx.x; i < ntok; i += kStageThreads) {
+    float tot = 0.0f;
+    for (int c = 0; c < nch; ++c) tot = tot + sumsq[i * nch + c];
+    inv_rms[i] = rsqrtf(tot * inv_hidden + eps);
+  }
+  __syncthreads();
+
+  for (int x = threadIdx.x; x < n * kWaveLanes; x += kStageThreads) {
+    const int j = x / kWaveLanes;
+    const int i = j / nch;
+    const int colv = (j - i * nch) * kWaveLanes + (x - j * kWaveLanes);
+    if (colv < a.h8) {
+      const int64_t o = (int64_t)(t0 + b + i * nb) * a.h8 + colv;
+      const u32x4 rb = stage_r[x];
+      __builtin_nontemporal_store(rb, residual_out + o);
+      float xv[8], g[8], nv[8];
+      unpack8(rb, xv);
+      unpack8(gamma[colv], g);
+      const float inv = inv_rms[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) nv[e] = (xv[e] * inv) * g[e];
+      __builtin_nontemporal_store(pack8_rne(nv), normed + o);
+    }
+  }
+  report_out_of_range(a, oob);
 }
 
 // ------------------------------------------------------- UE8M0 / E4M3 quant
@@ -231,19 +398,24 @@ __global__ void __launch_bounds__(kWavesPerBlock * kWaveLanes)
 finalize_quant_kernel(GatherArgs a, u32x2* __restrict__ out_q, uint8_t* __restrict__ scale) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  const int unit = (int)blockIdx.x * kWavesPerBlock + wave;
-  if ((int64_t)unit >= (int64_t)a.tokens * a.nchunks) return;   // whole waves
+  // as finalize_kernel: waves past the last unit redo it and store nothing
+  const int units = a.tokens * a.nchunks;
+  const bool live = (int)blockIdx.x * kWavesPerBlock + wave < units;
+  const int unit = live ? (int)blockIdx.x * kWavesPerBlock + wave : units - 1;
   const int t = unit / a.nchunks;
   const int colv = (unit - t * a.nchunks) * kWaveLanes + lane;
-  const bool active = colv < a.h8;       // h8 % 16 == 0: whole DPP rows agree
-  const int64_t col = active ? colv : a.h8 - 1;
+  const bool active = live && colv < a.h8;   // h8 % 16 == 0: whole DPP rows agree
+  const int64_t col = colv < a.h8 ? colv : a.h8 - 1;
 
   const Side d = load_side(a, t, col, nullptr);
-  int32_t row[KMAX];
-  float w[KMAX];
-  load_route<KMAX, EXACT>(a, t, row, w);
+  Gathered<KMAX> g;
+  issue_gather<KMAX, EXACT>(a, t, col, g);
+  load_now(out_q);         // after every load: the asm counts as a memory access
+  load_now(scale);
+  load_now(a.err);
   float acc[8];
-  finalize_acc<KMAX, EXACT>(a, col, row, w, d, false, acc);
+  reduce_rows<KMAX, EXACT>(a, g.row, g.v, g.w, d, false, acc);
+  const bool oob = g.oob;
 
   const u32x4 y = pack8_rne(acc);                    // the bf16 finalize result
   const uint32_t amax = row16_max(active ? absmax8_bits(y) : 0u);
@@ -253,70 +425,145 @@ finalize_quant_kernel(GatherArgs a, u32x2* __restrict__ out_q, uint8_t* __restri
     __builtin_nontemporal_store(q, out_q + (int64_t)t * a.h8 + colv);
     if ((lane & 15) == 0) scale[(int64_t)t * (a.h8 >> 4) + (colv >> 4)] = (uint8_t)(ex + 127);
   }
+  report_out_of_range(a, oob);
 }
 
 // ------------------------------------- UE8M0 / E4M3 quant, staged output
+
+// Where the staged quant kernel's units go. A launch covers the tokens
+// [t0, t1); its workgroups form g groups of wpx = gridDim.x / g, group x
+// being the workgroups b with b % g == x, which the dispatcher places on one
+// XCD (workgroups go to the XCDs round-robin). Tokens are dealt to the
+// groups in blocks of kXcdTokenBlock (block m to group m % g) for as many
+// full rounds of g blocks as the launch holds, and the remaining tokens one
+// by one (token r of the rest to group r % g), so no group holds more than
+// ceil((t1 - t0) / g) tokens. Within its group, workgroup w = b / g takes the
+// group's units lu = w + j * wpx, j = 0, 1, ..., unit lu being chunk
+// lu % nchunks of the group's token lu / nchunks. All chunks of a token, and
+// so all the scale bytes of a block of 16 tokens (at H = 7168, 896 bytes:
+// seven whole 128-byte lines), are written through one XCD's L2, which
+// merges them into whole lines.
+struct TokenGroups {
+  int t0;      // first token of the launch
+  int g;       // groups
+  int x;       // this workgroup's group
+  int full;    // full rounds of g blocks
+};
+
+// Token of the group-local token index lt.
+__device__ __forceinline__ int group_token(const TokenGroups& p, int lt) {
+  const int in_full = p.full * kXcdTokenBlock;
+  return lt < in_full
+             ? p.t0 + ((lt / kXcdTokenBlock) * p.g + p.x) * kXcdTokenBlock + lt % kXcdTokenBlock
+             : p.t0 + in_full * p.g + p.x + (lt - in_full) * p.g;
+}
+
+// The quantized output of one unit: the bf16 finalize result y of the
+// lane's 8 columns, its 1 x 128 block's UE8M0 exponent (one DPP row holds a
+// block) and the E4M3 codes of y / 2^e.
+__device__ __forceinline__ u32x2 quant_unit(const float acc[8], bool active, int& ex) {
+  const u32x4 y = pack8_rne(acc);
+  const uint32_t amax = row16_max(active ? absmax8_bits(y) : 0u);
+  ex = ue8m0_exponent(amax);
+  return e4m3x8_scaled(y, ue8m0_scale(ex));
+}
 
 // The same result as finalize_quant_kernel, for large grids. The quant
 // output is 5% of the launch's bytes, but written in the middle of the
 // gathers it costs about 15% of the time: the DRAM turns between reads and
 // writes all through the launch. Here every write waits until the reads are
-// done. One workgroup per CU (kStageThreads lanes) owns the CU's whole LDS
-// and processes the units u0 + b + j * gridDim.x of [u0, u1) for
-// j = 0, 1, ...: its waves take the next j from an LDS counter (so the
-// workgroup's waves finish together), keep the E4M3 codes and scale bytes of
-// unit j in LDS slot j (j < kStageUnits) or, beyond that, in one of R
-// register slots of the wave, and only after the workgroup's last gather
-// write them all (the workgroup barrier also keeps the compiler from moving
-// any store up into the gather loop). The launch start aligns the read
-// phases of all CUs, so the chip's writes come in the last stretch of the
-// launch, while the slowest CUs finish reading, instead of all through it.
-// (No grid-wide barrier: each workgroup only writes its own units.) The host
-// sizes a launch so that every workgroup's units fit,
+// done. The first `staged` workgroups (one per CU, kStageThreads lanes each)
+// own a CU's whole LDS and process their units (placed as TokenGroups says,
+// over staged / groups workgroups per group) in order j = 0, 1, ...: their
+// waves take the next j from an LDS counter (so a workgroup's waves finish
+// together), keep the E4M3 codes and scale bytes of unit j in LDS slot j
+// (j < kStageUnits) or, beyond that, in one of R register slots of the wave,
+// and only after the workgroup's last gather write them all (the workgroup
+// barrier also keeps the compiler from moving any store up into the gather
+// loop). The launch start aligns the read phases of all CUs, so the chip's
+// writes come in the last stretch of the launch, while the slowest CUs
+// finish reading, instead of all through it. (No grid-wide barrier: each
+// workgroup only writes its own units.)
+// The last tail_percent of each group's units go to the workgroups after
+// the staged ones, kStageWaves units each (one per wave, written at
+// once). Each needs a whole CU's LDS too, so the dispatcher starts them on
+// the CUs whose staged workgroup finished first, which evens out the ends of
+// the CUs' read phases; tail workgroup b goes to the XCD of group
+// (b - staged) % groups, as its group's staged workgroups do.
+// The host sizes a launch so that every staged workgroup's units fit,
 // n <= kStageUnits + kStageWaves * R; a unit that still found no slot would
 // be written at once, so no sizing can drop one.
 template <int KMAX, bool EXACT, int R>
 __global__ void __launch_bounds__(kStageThreads)
 finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
-                             uint8_t* __restrict__ scale, int u0, int u1) {
+                             uint8_t* __restrict__ scale, int t0, int t1, int groups,
+                             int staged, int tail_percent) {
   __shared__ u32x2 stage_q[kStageUnits * kWaveLanes];
   __shared__ uint32_t stage_e[kStageUnits];     // four scale bytes per unit
   __shared__ int next_j;
   constexpr int RS = R > 0 ? R : 1;
-  const int nb = (int)gridDim.x;
   const int b = (int)blockIdx.x;
-  const int n = u1 - u0 > b ? (u1 - u0 - b + nb - 1) / nb : 0;   // this workgroup's units
-  const int nl = n < kStageUnits ? n : kStageUnits;               // of them staged in LDS
   const int lane = threadIdx.x & 63;
+  const int wpx = staged / groups;
+  const bool tail_wg = b >= staged;
+  TokenGroups p;
+  p.t0 = t0;
+  p.g = groups;
+  p.x = (tail_wg ? b - staged : b) % groups;
+  p.full = (t1 - t0) / (groups * kXcdTokenBlock);
+  const int rest = (t1 - t0) - p.full * groups * kXcdTokenBlock;
+  const int group_tokens = p.full * kXcdTokenBlock + (rest > p.x ? (rest - p.x + groups - 1) / groups : 0);
+  const int group_units = group_tokens * a.nchunks;
+  const int static_units = group_units - group_units * tail_percent / 100;
+
+  if (tail_wg) {                         // one unit per wave, written at once
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lu = static_units + ((b - staged) / groups) * kStageWaves + wave;
+    if (lu >= group_units) return;
+    const int lt = lu / a.nchunks;
+    const int t = group_token(p, lt);
+    const int colv = (lu - lt * a.nchunks) * kWaveLanes + lane;
+    const bool active = colv < a.h8;
+    const int64_t col = active ? colv : a.h8 - 1;
+    const Side d = load_side(a, t, col, nullptr);
+    float acc[8];
+    const bool oob = finalize_vector<KMAX, EXACT>(a, t, col, d, false, acc);
+    int ex;
+    const u32x2 q = quant_unit(acc, active, ex);
+    if (active) {
+      __builtin_nontemporal_store(q, out_q + (int64_t)t * a.h8 + colv);
+      if ((lane & 15) == 0) scale[(int64_t)t * (a.h8 >> 4) + (colv >> 4)] = (uint8_t)(ex + 127);
+    }
+    report_out_of_range(a, oob);
+    return;
+  }
+
+  const int w = b / groups;
+  const int n = static_units > w ? (static_units - w + wpx - 1) / wpx : 0;   // this workgroup's units
+  const int nl = n < kStageUnits ? n : kStageUnits;                         // of them staged in LDS
   if (threadIdx.x == 0) next_j = 0;
   __syncthreads();
 
-  u32x2 rq[RS];            // register slots: codes, scale byte, unit index
+  u32x2 rq[RS];            // register slots: codes, scale byte, group-local unit
   uint32_t re[RS];
   int ru[RS];
   int cnt = 0;             // register slots in use (wave-uniform)
-  for (;;) {
-    int j = 0;
-    if (lane == 0) j = atomicAdd(&next_j, 1);
-    j = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(j, 0));
-    if (j >= n) break;
-    const int unit = u0 + b + j * nb;
-    const int t = unit / a.nchunks;
-    const int colv = (unit - t * a.nchunks) * kWaveLanes + lane;
+  bool oob = false;        // a slot of one of the wave's tokens was out of range
+  for (int it = 0; it < n; ++it) {
+    const int j = next_unit(&next_j);
+    if ((unsigned)j >= (unsigned)n) break;
+    const int lu = w + j * wpx;
+    const int lt = lu / a.nchunks;
+    const int t = group_token(p, lt);
+    const int colv = (lu - lt * a.nchunks) * kWaveLanes + lane;
     const bool active = colv < a.h8;
     const int64_t col = active ? colv : a.h8 - 1;
 
     const Side d = load_side(a, t, col, nullptr);
-    int32_t row[KMAX];
-    float w[KMAX];
-    load_route<KMAX, EXACT>(a, t, row, w);
     float acc[8];
-    finalize_acc<KMAX, EXACT>(a, col, row, w, d, false, acc);
-
-    const u32x4 y = pack8_rne(acc);
-    const uint32_t amax = row16_max(active ? absmax8_bits(y) : 0u);
-    const int ex = ue8m0_exponent(amax);
-    const u32x2 q = e4m3x8_scaled(y, ue8m0_scale(ex));
+    oob = finalize_vector<KMAX, EXACT>(a, t, col, d, false, acc) || oob;
+    int ex;
+    const u32x2 q = quant_unit(acc, active, ex);
     if (j < nl) {
       stage_q[j * kWaveLanes + lane] = q;
       if ((lane & 15) == 0) reinterpret_cast<uint8_t*>(&stage_e[j])[lane >> 4] = (uint8_t)(ex + 127);
@@ -326,7 +573,7 @@ finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
         if (cnt == s) {
           rq[s] = q;
           re[s] = (uint32_t)(ex + 127);
-          ru[s] = unit;
+          ru[s] = lu;
         }
       ++cnt;
     } else if (active) {
@@ -342,8 +589,9 @@ finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
 #pragma unroll
   for (int s = 0; s < RS; ++s) {
     if (R > 0 && s < cnt) {
-      const int t = ru[s] / a.nchunks;
-      const int colv = (ru[s] - t * a.nchunks) * kWaveLanes + lane;
+      const int lt = ru[s] / a.nchunks;
+      const int t = group_token(p, lt);
+      const int colv = (ru[s] - lt * a.nchunks) * kWaveLanes + lane;
       if (colv < a.h8) {
         __builtin_nontemporal_store(rq[s], out_q + (int64_t)t * a.h8 + colv);
         if ((lane & 15) == 0) scale[(int64_t)t * (a.h8 >> 4) + (colv >> 4)] = (uint8_t)re[s];
@@ -353,9 +601,10 @@ finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
   for (int x = threadIdx.x; x < nl * kWaveLanes; x += kStageThreads) {
     const int j = x / kWaveLanes;
     const int l = x - j * kWaveLanes;
-    const int unit = u0 + b + j * nb;
-    const int t = unit / a.nchunks;
-    const int colv = (unit - t * a.nchunks) * kWaveLanes + l;
+    const int lu = w + j * wpx;
+    const int lt = lu / a.nchunks;
+    const int t = group_token(p, lt);
+    const int colv = (lu - lt * a.nchunks) * kWaveLanes + l;
     if (colv < a.h8) {
       __builtin_nontemporal_store(stage_q[x], out_q + (int64_t)t * a.h8 + colv);
       if ((l & 15) == 0)
@@ -363,6 +612,7 @@ finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
             reinterpret_cast<const uint8_t*>(&stage_e[j])[l >> 4];
     }
   }
+  report_out_of_range(a, oob);
 }
 
 // ---------------------------------------------- plain finalize, staged output
@@ -371,11 +621,14 @@ finalize_quant_staged_kernel(GatherArgs a, u32x2* __restrict__ out_q,
 // finalize_quant_staged_kernel above (one workgroup per CU, units
 // u0 + b + j * gridDim.x taken from an LDS counter, writes after the
 // workgroup's last gather). A unit's output is its 1 KiB of bf16: LDS holds
-// kStagePlainUnits of them, each wave R more in registers. The output is 10%
-// of the plain finalize's bytes (k = 8), so keeping it out of the read phase
-// gains more than for the quant output.
-template <int KMAX, bool EXACT, int R>
-__global__ void __launch_bounds__(kStageThreads)
+// kStagePlainUnits of them, each of the WAVES waves R more in registers. The
+// output is 10% of the plain finalize's bytes (k = 8), so keeping it out of
+// the read phase gains more than for the quant output. With 12 waves a wave
+// may use up to 168 VGPRs (3 waves per SIMD), room for 25 register slots:
+// 159 + 12 * 25 = 459 units per CU hold a 8192-token, H = 7168 call (448
+// units per CU) in one launch.
+template <int KMAX, bool EXACT, int R, int WAVES>
+__global__ void __launch_bounds__(WAVES * kWaveLanes)
 finalize_staged_kernel(GatherArgs a, u32x4* __restrict__ out, int u0, int u1) {
   __shared__ u32x4 stage_o[kStagePlainUnits * kWaveLanes];
   __shared__ int next_j;
@@ -391,36 +644,34 @@ finalize_staged_kernel(GatherArgs a, u32x4* __restrict__ out, int u0, int u1) {
   u32x4 ro[RS];            // register slots: bf16 output vector, unit index
   int ru[RS];
   int cnt = 0;             // register slots in use (wave-uniform)
-  for (;;) {
-    int j = 0;
-    if (lane == 0) j = atomicAdd(&next_j, 1);
-    j = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(j, 0));
-    if (j >= n) break;
+  bool oob = false;        // a slot of one of the wave's tokens was out of range
+  for (int it = 0; it < n; ++it) {
+    const int j = next_unit(&next_j);
+    if ((unsigned)j >= (unsigned)n) break;
     const int unit = u0 + b + j * nb;
     const int t = unit / a.nchunks;
     const int colv = (unit - t * a.nchunks) * kWaveLanes + lane;
     const int64_t col = colv < a.h8 ? colv : a.h8 - 1;
 
     const Side d = load_side(a, t, col, nullptr);
-    int32_t row[KMAX];
-    float w[KMAX];
-    load_route<KMAX, EXACT>(a, t, row, w);
     float acc[8];
-    finalize_acc<KMAX, EXACT>(a, col, row, w, d, false, acc);
+    oob = finalize_vector<KMAX, EXACT>(a, t, col, d, false, acc) || oob;
     const u32x4 y = pack8_rne(acc);
-    if (j < nl) {
-      stage_o[j * kWaveLanes + lane] = y;
-    } else if (R > 0 && cnt < R) {
+    if (j < nl) stage_o[j * kWaveLanes + lane] = y;
+    // Past the LDS slots, slot 0 of the registers takes the unit and the
+    // others move down one; a branch-free select, top slot first, so the
+    // update needs no second copy of the slots.
+    const bool take = R > 0 && j >= nl && cnt < R;
 #pragma unroll
-      for (int s = 0; s < RS; ++s)
-        if (cnt == s) {
-          ro[s] = y;
-          ru[s] = unit;
-        }
-      ++cnt;
-    } else if (colv < a.h8) {
-      __builtin_nontemporal_store(y, out + (int64_t)t * a.h8 + colv);   // no slot left
+    for (int s = RS - 1; s > 0; --s) {
+      ro[s] = take ? ro[s - 1] : ro[s];
+      ru[s] = take ? ru[s - 1] : ru[s];
     }
+    ro[0] = take ? y : ro[0];
+    ru[0] = take ? unit : ru[0];
+    cnt += take ? 1 : 0;
+    if (j >= nl && !take && colv < a.h8)
+      __builtin_nontemporal_store(y, out + (int64_t)t * a.h8 + colv);   // no slot left
   }
   __syncthreads();         // every unit of the workgroup is staged or written
 
@@ -432,7 +683,7 @@ finalize_staged_kernel(GatherArgs a, u32x4* __restrict__ out, int u0, int u1) {
       if (colv < a.h8) __builtin_nontemporal_store(ro[s], out + (int64_t)t * a.h8 + colv);
     }
   }
-  for (int x = threadIdx.x; x < nl * kWaveLanes; x += kStageThreads) {
+  for (int x = threadIdx.x; x < nl * kWaveLanes; x += WAVES * kWaveLanes) {
     const int j = x / kWaveLanes;
     const int l = x - j * kWaveLanes;
     const int unit = u0 + b + j * nb;
@@ -440,6 +691,7 @@ finalize_staged_kernel(GatherArgs a, u32x4* __restrict__ out, int u0, int u1) {
     const int colv = (unit - t * a.nchunks) * kWaveLanes + l;
     if (colv < a.h8) __builtin_nontemporal_store(stage_o[x], out + (int64_t)t * a.h8 + colv);
   }
+  report_out_of_range(a, oob);
 }
 
 // ------------------------------------------------------------ packed decode
@@ -546,27 +798,20 @@ unsigned int plain_blocks(const GatherArgs& a) {
 
 namespace {
 
-// CUs of the current device, or 0 if the runtime cannot say.
-int device_cus() {
-  int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  return ncu;
-}
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_cus[kMaxDevices];
 
-// Splits the grid's units into as few launches as hold every unit (a launch
-// covers at most ncu * (lds_units + kStageWaves * reg_units) of them), in
-// equal contiguous ranges, and calls launch(u0, u1, registers) for each;
-// `registers` says whether a workgroup's units can exceed lds_units (it then
-// needs the kernel with register slots).
+// Splits the grid's units into as few launches as hold every unit (a
+// workgroup holds at most lds_units + reg_capacity of them; see plan_staged)
+// and calls launch(u0, u1, registers) for each; `registers` says whether a
+// workgroup's units can exceed lds_units (it then needs the kernel with
+// register slots).
 template <typename F>
-hipError_t staged_launches(const GatherArgs& a, int ncu, int lds_units, int reg_units,
+hipError_t staged_launches(const GatherArgs& a, int ncu, int lds_units, int reg_capacity,
                            F&& launch) {
   const int64_t units = (int64_t)a.tokens * a.nchunks;
-  const int64_t per_launch_max = (int64_t)ncu * (lds_units + kStageWaves * reg_units);
-  const int64_t launches = (units + per_launch_max - 1) / per_launch_max;
-  const int64_t per_launch = (units + launches - 1) / launches;
+  const StagedPlan plan = plan_staged(units, ncu, lds_units + reg_capacity);
+  const int64_t per_launch = plan.per_launch;
   for (int64_t u0 = 0; u0 < units; u0 += per_launch) {
     const int64_t u1 = u0 + per_launch < units ? u0 + per_launch : units;
     const int64_t per_wg = (u1 - u0 + ncu - 1) / ncu;
@@ -579,48 +824,86 @@ hipError_t staged_launches(const GatherArgs& a, int ncu, int lds_units, int reg_
 
 template <int KM, bool EX>
 hipError_t launch_quant_staged(const GatherArgs& a, u32x2* q, uint8_t* scale, int ncu,
-                               hipStream_t stream) {
-  return staged_launches(a, ncu, kStageUnits, kStageRegUnits, [&](int u0, int u1, bool regs) {
+                               const StagedPlan& plan, int groups, hipStream_t stream) {
+  for (int64_t t0 = 0; t0 < a.tokens; t0 += plan.per_launch) {
+    const int64_t t1 = t0 + plan.per_launch < a.tokens ? t0 + plan.per_launch : a.tokens;
+    const bool regs = quant_launch_regs(t1 - t0, a.nchunks, ncu, groups);
+    const int pct = quant_launch_tail_percent(t1 - t0, a.nchunks, ncu);
+    const dim3 grid((unsigned)(ncu + quant_launch_tail_workgroups(t1 - t0, a.nchunks, groups, pct)));
     if (regs)
-      hipLaunchKernelGGL((finalize_quant_staged_kernel<KM, EX, kStageRegUnits>), dim3(ncu),
-                         dim3(kStageThreads), 0, stream, a, q, scale, u0, u1);
+      hipLaunchKernelGGL((finalize_quant_staged_kernel<KM, EX, kStageRegUnits>), grid,
+                         dim3(kStageThreads), 0, stream, a, q, scale, (int)t0, (int)t1, groups,
+                         ncu, pct);
     else
-      hipLaunchKernelGGL((finalize_quant_staged_kernel<KM, EX, 0>), dim3(ncu),
-                         dim3(kStageThreads), 0, stream, a, q, scale, u0, u1);
-  });
+      hipLaunchKernelGGL((finalize_quant_staged_kernel<KM, EX, 0>), grid, dim3(kStageThreads), 0,
+                         stream, a, q, scale, (int)t0, (int)t1, groups, ncu, pct);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int KM, bool EX>
-hipError_t launch_plain_staged(const GatherArgs& a, u32x4* o, int ncu, hipStream_t stream) {
-  return staged_launches(a, ncu, kStagePlainUnits, kStagePlainRegUnits,
-                         [&](int u0, int u1, bool regs) {
+hipError_t launch_plain_staged(const GatherArgs& a, u32x4* o, int ncu, const PlainChoice& c,
+                               hipStream_t stream) {
+  if (!c.wide)
+    return staged_launches(a, ncu, kStagePlainUnits, kStagePlainWaves * kStagePlainRegUnits,
+                           [&](int u0, int u1, bool regs) {
+      if (regs)
+        hipLaunchKernelGGL((finalize_staged_kernel<KM, EX, kStagePlainRegUnits, kStagePlainWaves>),
+                           dim3(ncu), dim3(kStagePlainWaves * kWaveLanes), 0, stream, a, o, u0,
+                           u1);
+      else
+        hipLaunchKernelGGL((finalize_staged_kernel<KM, EX, 0, kStagePlainWaves>), dim3(ncu),
+                           dim3(kStagePlainWaves * kWaveLanes), 0, stream, a, o, u0, u1);
+    });
+  constexpr int W = kStagePlainWideWaves;
+  constexpr int R = kStagePlainWideRegUnits;
+  return staged_launches(a, ncu, kStagePlainUnits, W * R, [&](int u0, int u1, bool regs) {
     if (regs)
-      hipLaunchKernelGGL((finalize_staged_kernel<KM, EX, kStagePlainRegUnits>), dim3(ncu),
-                         dim3(kStageThreads), 0, stream, a, o, u0, u1);
+      hipLaunchKernelGGL((finalize_staged_kernel<KM, EX, R, W>), dim3(ncu), dim3(W * kWaveLanes),
+                         0, stream, a, o, u0, u1);
     else
-      hipLaunchKernelGGL((finalize_staged_kernel<KM, EX, 0>), dim3(ncu),
-                         dim3(kStageThreads), 0, stream, a, o, u0, u1);
+      hipLaunchKernelGGL((finalize_staged_kernel<KM, EX, 0, W>), dim3(ncu), dim3(W * kWaveLanes),
+                         0, stream, a, o, u0, u1);
   });
 }
 
 }  // namespace
 
+// The count of each device is queried once and kept: it sizes the staged
+// kernels' grids.
+int device_cus(hipStream_t stream) {
+  int dev = -1;
+  if (stream == nullptr || hipStreamGetDevice(stream, &dev) != hipSuccess) {
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+  }
+  if (dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int known = g_device_cus[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
+  }
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < kMaxDevices && ncu > 0) g_device_cus[dev].store(ncu, std::memory_order_relaxed);
+  return ncu;
+}
+
 hipError_t launch_finalize(const Routed& r, uint16_t* out, hipStream_t stream) {
   const GatherArgs a = make_args(r);
   u32x4* o = reinterpret_cast<u32x4*>(out);
-  const int64_t units = (int64_t)a.tokens * a.nchunks;
-  if (a.k <= kStagedMaxTopK) {
-    const int ncu = device_cus();
-    if (ncu > 0 && units >= kStagedPlainFromUnitsPerCu * ncu) {
-      return dispatch_top_k(a.k, [&](auto km, auto ex) {
-        constexpr int KM = decltype(km)::value;
-        constexpr bool EX = decltype(ex)::value;
-        if constexpr (KM <= kStagedMaxTopK)
-          return launch_plain_staged<KM, EX>(a, o, ncu, stream);
-        else
-          return hipErrorInvalidValue;   // not reached: top_k <= 8 dispatches KM <= 8
-      });
-    }
+  const int ncu = a.k <= kStagedMaxTopK ? device_cus(stream) : 0;
+  const PlainChoice c = plain_choice(a.tokens, r.hidden, a.k, ncu);
+  if (c.staged) {
+    return dispatch_top_k(a.k, [&](auto km, auto ex) {
+      constexpr int KM = decltype(km)::value;
+      constexpr bool EX = decltype(ex)::value;
+      if constexpr (KM <= kStagedMaxTopK)
+        return launch_plain_staged<KM, EX>(a, o, ncu, c, stream);
+      else
+        return hipErrorInvalidValue;   // not reached: top_k <= 8 dispatches KM <= 8
+    });
   }
   const size_t lds = stream_cap_lds((int64_t)a.tokens * a.nchunks);
   return dispatch_top_k(a.k, [&](auto km, auto ex) {
@@ -637,31 +920,45 @@ hipError_t launch_finalize_rmsnorm(const Routed& r, const uint16_t* residual,
                                    uint16_t* residual_out, uint16_t* normed,
                                    hipStream_t stream) {
   const GatherArgs a = make_args(r);
-  // One thread per 16-byte column vector (one wave per 512-column chunk) up
-  // to 16 waves; from kNormHalfWidthFrom tokens on, half as many waves with
-  // two vectors per thread when the chunk count is even.
-  int threads = a.nchunks * kWaveLanes;
-  if (a.tokens >= kNormHalfWidthFrom && a.nchunks % 2 == 0) threads /= 2;
-  if (threads > kNormMaxThreads) threads = kNormMaxThreads;
-  const int cpt = (a.h8 + threads - 1) / threads;   // 1 or 2 (hidden <= 16384)
-  // Two vectors per lane: reserve LDS (unused by the kernel) so that at most
-  // kNorm2MaxWavesPerCu waves are resident per CU; a workgroup too large for
-  // two to fit needs no reservation.
-  const int norm2_blocks = kNorm2MaxWavesPerCu / (threads / kWaveLanes);
-  const size_t lds2 = norm2_blocks >= 2 ? lds_for_blocks_per_cu(norm2_blocks) : 0;
   const float inv_hidden = 1.0f / (float)r.hidden;
   const u32x4* res = reinterpret_cast<const u32x4*>(residual);
   const u32x4* gam = reinterpret_cast<const u32x4*>(gamma);
   u32x4* ro = reinterpret_cast<u32x4*>(residual_out);
   u32x4* nm = reinterpret_cast<u32x4*>(normed);
+  const int ncu = a.k <= kStagedMaxTopK ? device_cus(stream) : 0;
+  const RmsChoice c = rmsnorm_choice(a.tokens, r.hidden, a.k, ncu);
+  if (c.staged) {
+    return dispatch_top_k(a.k, [&](auto km, auto ex) {
+      constexpr int KM = decltype(km)::value;
+      constexpr bool EX = decltype(ex)::value;
+      if constexpr (KM <= kStagedMaxTopK) {
+        for (int64_t t0 = 0; t0 < a.tokens; t0 += c.plan.per_launch) {
+          const int64_t t1 = t0 + c.plan.per_launch < a.tokens ? t0 + c.plan.per_launch : a.tokens;
+          hipLaunchKernelGGL((finalize_rmsnorm_staged_kernel<KM, EX>), dim3(ncu),
+                             dim3(kStageThreads), 0, stream, a, res, gam, eps, inv_hidden, ro,
+                             nm, (int)t0, (int)t1);
+          const hipError_t e = hipGetLastError();
+          if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+      } else {
+        return hipErrorInvalidValue;   // not reached: top_k <= 8 dispatches KM <= 8
+      }
+    });
+  }
+  // Two vectors per lane: reserve LDS (unused by the kernel) so that at most
+  // kNorm2MaxWavesPerCu waves are resident per CU; a workgroup too large for
+  // two to fit needs no reservation.
+  const int norm2_blocks = kNorm2MaxWavesPerCu / (c.threads / kWaveLanes);
+  const size_t lds2 = norm2_blocks >= 2 ? lds_for_blocks_per_cu(norm2_blocks) : 0;
   return dispatch_top_k(a.k, [&](auto km, auto ex) {
     constexpr int KM = decltype(km)::value;
     constexpr bool EX = decltype(ex)::value;
-    if (cpt == 1)
-      hipLaunchKernelGGL((finalize_rmsnorm_kernel<KM, EX, 1>), dim3(a.tokens), dim3(threads),
+    if (c.cpt == 1)
+      hipLaunchKernelGGL((finalize_rmsnorm_kernel<KM, EX, 1>), dim3(a.tokens), dim3(c.threads),
                          0, stream, a, res, gam, eps, inv_hidden, ro, nm);
     else
-      hipLaunchKernelGGL((finalize_rmsnorm_kernel<KM, EX, 2>), dim3(a.tokens), dim3(threads),
+      hipLaunchKernelGGL((finalize_rmsnorm_kernel<KM, EX, 2>), dim3(a.tokens), dim3(c.threads),
                          lds2, stream, a, res, gam, eps, inv_hidden, ro, nm);
     return hipGetLastError();
   });
@@ -672,19 +969,17 @@ hipError_t launch_finalize_quant(const Routed& r, uint8_t* out_e4m3, uint8_t* sc
                                  hipStream_t stream) {
   const GatherArgs a = make_args(r);
   u32x2* q = reinterpret_cast<u32x2*>(out_e4m3);
-  const int64_t units = (int64_t)a.tokens * a.nchunks;
-  if (a.k <= kStagedMaxTopK) {
-    const int ncu = device_cus();
-    if (ncu > 0 && units >= kStagedFromUnitsPerCu * ncu) {
-      return dispatch_top_k(a.k, [&](auto km, auto ex) {
-        constexpr int KM = decltype(km)::value;
-        constexpr bool EX = decltype(ex)::value;
-        if constexpr (KM <= kStagedMaxTopK)
-          return launch_quant_staged<KM, EX>(a, q, scale_e8m0, ncu, stream);
-        else
-          return hipErrorInvalidValue;   // not reached: top_k <= 8 dispatches KM <= 8
-      });
-    }
+  const int ncu = a.k <= kStagedMaxTopK ? device_cus(stream) : 0;
+  const QuantChoice c = quant_choice(a.tokens, r.hidden, a.k, ncu);
+  if (c.staged) {
+    return dispatch_top_k(a.k, [&](auto km, auto ex) {
+      constexpr int KM = decltype(km)::value;
+      constexpr bool EX = decltype(ex)::value;
+      if constexpr (KM <= kStagedMaxTopK)
+        return launch_quant_staged<KM, EX>(a, q, scale_e8m0, ncu, c.plan, c.groups, stream);
+      else
+        return hipErrorInvalidValue;   // not reached: top_k <= 8 dispatches KM <= 8
+    });
   }
   // Large launches reserve LDS (unused by the kernel) to hold 4 workgroups
   // per CU instead of 8: measured 1-2% faster from about a thousand tokens

@@ -8,6 +8,7 @@
 // graph capture and never grow them inside: "[Kimi K2.5] Fuse deferred MoE
 // finalize into next-layer AR + residual + RMSNorm", Key modifications).
 
+#include <cstdio>
 #include <type_traits>
 
 #include "moef_internal.h"
@@ -136,9 +137,80 @@ int act_quant(const uint16_t* x, int64_t num_tokens, int64_t hidden, uint8_t* ou
 
 }  // namespace
 
+namespace moef {
+
+// The kernel names below follow the form profilers print template instances
+// in ("name<8, true, 12>"), so a benchmark can find them in a trace.
+void describe_finalize(int op, int64_t tokens, int64_t hidden, int top_k, int ncu, char* buf,
+                       int64_t len) {
+  const TopKChoice k = top_k_choice(top_k);
+  const char* ex = k.exact ? "true" : "false";
+  const int64_t nch = nchunks_of(hidden);
+  const int64_t one_wave_blocks = (tokens * nch + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (op == 0) {
+    const PlainChoice c = plain_choice(tokens, hidden, top_k, ncu);
+    if (c.staged) {
+      const int waves = c.wide ? kStagePlainWideWaves : kStagePlainWaves;
+      const int reg = c.wide ? kStagePlainWideRegUnits : kStagePlainRegUnits;
+      const bool regs = (c.plan.per_launch + ncu - 1) / ncu > kStagePlainUnits;
+      snprintf(buf, (size_t)len, "finalize_staged_kernel<%d, %s, %d, %d> launches=%lld grid=%dx%d",
+               k.kmax, ex, regs ? reg : 0, waves, (long long)c.plan.launches, ncu,
+               waves * kWaveLanes);
+    } else {
+      snprintf(buf, (size_t)len, "finalize_kernel<%d, %s> launches=1 grid=%lldx%d", k.kmax, ex,
+               (long long)one_wave_blocks, kWavesPerBlock * kWaveLanes);
+    }
+  } else if (op == 1) {
+    const RmsChoice c = rmsnorm_choice(tokens, hidden, top_k, ncu);
+    if (c.staged)
+      snprintf(buf, (size_t)len, "finalize_rmsnorm_staged_kernel<%d, %s> launches=%lld grid=%dx%d",
+               k.kmax, ex, (long long)c.plan.launches, ncu, kStageThreads);
+    else
+      snprintf(buf, (size_t)len, "finalize_rmsnorm_kernel<%d, %s, %d> launches=1 grid=%lldx%d",
+               k.kmax, ex, c.cpt, (long long)tokens, c.threads);
+  } else {
+    const QuantChoice c = quant_choice(tokens, hidden, top_k, ncu);
+    if (c.staged) {
+      const int64_t tl = c.plan.per_launch < tokens ? c.plan.per_launch : tokens;
+      const bool regs = quant_launch_regs(tl, nch, ncu, c.groups);
+      const int pct = quant_launch_tail_percent(tl, nch, ncu);
+      const int64_t tail = quant_launch_tail_workgroups(tl, nch, c.groups, pct);
+      snprintf(buf, (size_t)len,
+               "finalize_quant_staged_kernel<%d, %s, %d> launches=%lld grid=%lldx%d groups=%d "
+               "tail=%d%%",
+               k.kmax, ex, regs ? kStageRegUnits : 0, (long long)c.plan.launches,
+               (long long)(ncu + tail), kStageThreads, c.groups, pct);
+    } else {
+      snprintf(buf, (size_t)len, "finalize_quant_kernel<%d, %s> launches=1 grid=%lldx%d", k.kmax,
+               ex, (long long)one_wave_blocks, kWavesPerBlock * kWaveLanes);
+    }
+  }
+}
+
+}  // namespace moef
+
 extern "C" {
 
 int moe_finalize_abi_version(void) { return MOEF_ABI_VERSION; }
+
+int moe_finalize_describe_launch(int32_t op, int64_t num_tokens, int64_t hidden, int32_t top_k,
+                                 void* stream, char* buf, int64_t buf_len) {
+  if (buf == nullptr || buf_len < 1) return MOEF_ERR_NULL_POINTER;
+  buf[0] = '\0';
+  if (op < MOEF_OP_FINALIZE || op > MOEF_OP_QUANT_UE8M0) return MOEF_ERR_BAD_SHAPE;
+  bool noop = false;
+  const int st = check_shape(0, num_tokens, hidden, top_k, &noop);
+  if (st != MOEF_OK) return st;
+  if (op == MOEF_OP_RESIDUAL_RMSNORM && hidden > MOEF_MAX_HIDDEN_RMSNORM) return MOEF_ERR_UNSUPPORTED;
+  if (op == MOEF_OP_QUANT_UE8M0 && hidden % MOEF_QUANT_BLOCK != 0) return MOEF_ERR_UNSUPPORTED;
+  if (noop) {
+    snprintf(buf, (size_t)buf_len, "none (num_tokens == 0)");
+    return MOEF_OK;
+  }
+  const int ncu = top_k <= moef::kStagedMaxTopK ? moef::device_cus(static_cast<hipStream_t>(stream)) : 0;
+  moef::describe_finalize(op, num_tokens, hidden, top_k, ncu, buf, buf_len);
+  return MOEF_OK;
+}
 
 const char* moe_finalize_status_string(int status) {
   switch (status) {

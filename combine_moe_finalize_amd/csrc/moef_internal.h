@@ -100,16 +100,207 @@ constexpr int kStageUnitBytes = kChunkCols + 4;        // E4M3 codes + 4 scale b
 constexpr int kStageUnits = (kLdsPerCu - 256) / kStageUnitBytes;   // 317
 constexpr int kStageRegUnits = 12;
 constexpr int64_t kStagedFromUnitsPerCu = 80;
+// From kStagedTailFromUnitsPerCu units per CU, the last kStagedTailPercent of
+// each group's units go to workgroups beyond the one per CU, one unit per
+// wave, which the dispatcher starts on the CUs that finish their share first
+// (finalize_quant_staged_kernel). Measured at H = 7168: T = 8192 (448 units
+// per CU) 172.4 -> 169.0 us; T = 2048 (112 per CU) 44.4 -> 44.8 us.
+constexpr int kStagedTailPercent = 5;
+constexpr int64_t kStagedTailFromUnitsPerCu = 256;
 constexpr int kStagedMaxTopK = 8;
 static_assert(kStageUnits * kStageUnitBytes + 4 <= kLdsPerCu, "staging fits the CU's LDS");
 // The plain finalize stages the same way: 1 KiB of bf16 output per unit, 159
-// units in LDS and up to 8 more per wave in registers (four VGPRs each); used
-// from 48 units per CU (T = 878 at H = 7168 on 256 CUs), top_k <= 8.
+// units in LDS and more in registers (four VGPRs a unit). Workgroups of 16
+// waves hold 8 register slots a wave (287 units per CU); grids larger than
+// that take workgroups of 12 waves, whose waves may use 168 VGPRs, room for
+// 25 slots (459 units per CU: T = 8192 at H = 7168 in one launch, 180.4 us
+// against 184.4 for two 16-wave launches; at 224 units per CU the 16-wave
+// layout was 1% faster). Used from 48 units per CU (T = 878 at H = 7168 on
+// 256 CUs), top_k <= 8.
 constexpr int kStagePlainUnitBytes = kChunkCols * 2;
 constexpr int kStagePlainUnits = (kLdsPerCu - 256) / kStagePlainUnitBytes;   // 159
+constexpr int kStagePlainWaves = 16;
 constexpr int kStagePlainRegUnits = 8;
+constexpr int kStagePlainWideWaves = 12;
+constexpr int kStagePlainWideRegUnits = 25;
 constexpr int64_t kStagedPlainFromUnitsPerCu = 48;
 static_assert(kStagePlainUnits * kStagePlainUnitBytes + 4 <= kLdsPerCu, "staging fits the LDS");
+// The staged quant kernel deals tokens to groups of workgroups, one group per
+// XCD, in blocks of kXcdTokenBlock tokens, so that all scale bytes of a block
+// are written through one XCD's L2 (finalize_quant_staged_kernel). MI355X
+// has 8 XCDs and hands workgroups to them round-robin; a CU count that 8
+// does not divide (a partitioned device) takes one group.
+constexpr int kXcds = 8;
+constexpr int kXcdTokenBlock = 16;
+inline int staged_quant_groups(int ncu) { return ncu % kXcds == 0 ? kXcds : 1; }
+
+// The staged quant kernel's launch plan, in whole tokens: a launch over Tl
+// tokens gives each of its `groups` groups of ncu / groups workgroups at most
+// ceil(Tl / groups) tokens, so a workgroup holds at most
+// ceil(ceil(Tl / groups) * nchunks / (ncu / groups)) units. Launches are as
+// few as keep that within per_wg_max, and as long as a multiple of
+// groups * kXcdTokenBlock tokens where that fits. No launch (0) when not one
+// token per group fits.
+struct StagedPlan;
+inline StagedPlan plan_staged_tokens(int64_t tokens, int64_t nchunks, int ncu, int groups,
+                                     int64_t per_wg_max);
+
+// The residual + RMSNorm epilogue stages the same way
+// (finalize_rmsnorm_staged_kernel): a workgroup owns whole tokens, and each
+// of their (token, chunk) units keeps 1 KiB of bf16 residual_out plus its
+// sum of squares in LDS (4 more bytes per unit hold the per-token 1 / rms),
+// 158 units per workgroup and launch, 11 tokens at H = 7168; larger grids
+// take several launches. Used from kStagedRmsFromUnitsPerCu units per CU,
+// top_k <= 8.
+constexpr int kStageRmsUnitBytes = kChunkCols * 2 + 8;
+constexpr int kStageRmsUnits = (kLdsPerCu - 256) / kStageRmsUnitBytes;     // 158
+constexpr int64_t kStagedRmsFromUnitsPerCu = 40;
+static_assert(kStageRmsUnits * kStageRmsUnitBytes + 4 <= kLdsPerCu, "staging fits the LDS");
+static_assert(kStageRmsUnits / (MOEF_MAX_HIDDEN_RMSNORM / kChunkCols) >= 1,
+              "a workgroup holds at least one token of the largest hidden size");
+
+// Launch plan of a staged kernel: `items` (units, or tokens for the RMSNorm
+// epilogue) in as few launches as keep every workgroup within `per_wg_max`
+// items, each launch a contiguous range [r * per_launch, min(items, (r + 1)
+// * per_launch)) spread round-robin over `ncu` workgroups (item i of the
+// range to workgroup i % ncu), so a workgroup holds at most
+// ceil(per_launch / ncu) <= per_wg_max items.
+struct StagedPlan {
+  int64_t launches;
+  int64_t per_launch;
+};
+inline StagedPlan plan_staged(int64_t items, int ncu, int64_t per_wg_max) {
+  const int64_t cap = (int64_t)ncu * per_wg_max;
+  const int64_t launches = (items + cap - 1) / cap;
+  return StagedPlan{launches, launches > 0 ? (items + launches - 1) / launches : 0};
+}
+
+inline StagedPlan plan_staged_tokens(int64_t tokens, int64_t nchunks, int ncu, int groups,
+                                     int64_t per_wg_max) {
+  const int64_t wpx = ncu / groups;
+  const int64_t round = (int64_t)groups * kXcdTokenBlock;
+  int64_t tl_max = groups * ((per_wg_max * wpx) / nchunks);
+  if (tl_max >= round) tl_max = tl_max / round * round;
+  if (tl_max <= 0 || tokens <= 0) return StagedPlan{0, 0};
+  const int64_t launches = (tokens + tl_max - 1) / tl_max;
+  int64_t per = (tokens + launches - 1) / launches;
+  if (tl_max >= round) {
+    per = (per + round - 1) / round * round;
+    if (per > tl_max) per = tl_max;
+  }
+  return StagedPlan{(tokens + per - 1) / per, per};
+}
+
+// ---------------------------------------------------------- launch plans
+// The launchers' choices, shared with moe_finalize_describe_launch so that
+// what it reports is what they do. `ncu` is the CU count of the stream's
+// device; 0 (unknown) keeps every call on the one-wave-per-unit kernels.
+
+// The kernel instantiation a top_k runs: exact for 1, 2, 4, 6, 8, else the
+// next larger instantiation with a runtime bound (guarded).
+struct TopKChoice {
+  int kmax;
+  bool exact;
+};
+inline TopKChoice top_k_choice(int k) {
+  if (k == 1 || k == 2 || k == 4 || k == 6 || k == 8) return TopKChoice{k, true};
+  return TopKChoice{k <= 4 ? 4 : (k <= 8 ? 8 : 16), false};
+}
+
+inline int64_t nchunks_of(int64_t hidden) { return (hidden / kVecElems + kWaveLanes - 1) / kWaveLanes; }
+
+// The plain finalize: staged (16-wave layout, else the wide 12-wave one) or
+// one wave per unit.
+struct PlainChoice {
+  bool staged;
+  bool wide;
+  StagedPlan plan;      // units per launch
+};
+inline PlainChoice plain_choice(int64_t tokens, int64_t hidden, int top_k, int ncu) {
+  PlainChoice c{false, false, StagedPlan{1, 0}};
+  const int64_t units = tokens * nchunks_of(hidden);
+  if (top_k > kStagedMaxTopK || ncu <= 0 || units < kStagedPlainFromUnitsPerCu * ncu) return c;
+  c.staged = true;
+  c.wide = units > (int64_t)ncu * (kStagePlainUnits + kStagePlainWaves * kStagePlainRegUnits);
+  c.plan = plan_staged(units, ncu, kStagePlainUnits + (c.wide ? kStagePlainWideWaves * kStagePlainWideRegUnits
+                                                              : kStagePlainWaves * kStagePlainRegUnits));
+  return c;
+}
+
+// The residual + RMSNorm epilogue: staged (whole tokens per workgroup) or
+// one workgroup per token with `threads` lanes and cpt vectors per lane.
+struct RmsChoice {
+  bool staged;
+  StagedPlan plan;      // tokens per launch
+  int threads;
+  int cpt;
+};
+inline RmsChoice rmsnorm_choice(int64_t tokens, int64_t hidden, int top_k, int ncu) {
+  RmsChoice c{false, StagedPlan{1, 0}, 0, 0};
+  const int64_t nch = nchunks_of(hidden);
+  if (top_k <= kStagedMaxTopK && ncu > 0 && tokens * nch >= kStagedRmsFromUnitsPerCu * ncu) {
+    c.staged = true;
+    c.plan = plan_staged(tokens, ncu, kStageRmsUnits / nch);
+    return c;
+  }
+  // One thread per 16-byte column vector (one wave per 512-column chunk) up
+  // to 16 waves; from kNormHalfWidthFrom tokens on, half as many waves with
+  // two vectors per thread when the chunk count is even.
+  int threads = (int)nch * kWaveLanes;
+  if (tokens >= kNormHalfWidthFrom && nch % 2 == 0) threads /= 2;
+  if (threads > kNormMaxThreads) threads = kNormMaxThreads;
+  c.threads = threads;
+  c.cpt = (int)((hidden / kVecElems + threads - 1) / threads);   // 1 or 2 (hidden <= 16384)
+  return c;
+}
+
+// The UE8M0 finalize: staged (token groups per XCD, whole-token launches) or
+// one wave per unit.
+struct QuantChoice {
+  bool staged;
+  int groups;
+  StagedPlan plan;      // tokens per launch
+};
+inline QuantChoice quant_choice(int64_t tokens, int64_t hidden, int top_k, int ncu) {
+  QuantChoice c{false, 1, StagedPlan{1, 0}};
+  const int64_t nch = nchunks_of(hidden);
+  if (top_k > kStagedMaxTopK || ncu <= 0 || tokens * nch < kStagedFromUnitsPerCu * ncu) return c;
+  const int64_t cap = kStageUnits + kStageWaves * kStageRegUnits;
+  c.groups = staged_quant_groups(ncu);
+  c.plan = plan_staged_tokens(tokens, nch, ncu, c.groups, cap);
+  if (c.plan.launches == 0 && c.groups > 1) {
+    c.groups = 1;
+    c.plan = plan_staged_tokens(tokens, nch, ncu, c.groups, cap);
+  }
+  c.staged = c.plan.launches > 0;
+  return c;
+}
+// Of one staged quant launch over tl tokens: whether a workgroup can hold
+// more units than the LDS slots (the kernel with register slots), and the
+// tail percentage.
+inline bool quant_launch_regs(int64_t tl, int64_t nchunks, int ncu, int groups) {
+  const int64_t wpx = ncu / groups;
+  return ((tl + groups - 1) / groups * nchunks + wpx - 1) / wpx > kStageUnits;
+}
+inline int quant_launch_tail_percent(int64_t tl, int64_t nchunks, int ncu) {
+  return tl * nchunks >= kStagedTailFromUnitsPerCu * ncu ? kStagedTailPercent : 0;
+}
+inline int64_t quant_launch_tail_workgroups(int64_t tl, int64_t nchunks, int groups, int pct) {
+  const int64_t group_units = (tl + groups - 1) / groups * nchunks;
+  return groups * ((group_units * pct / 100 + kStageWaves - 1) / kStageWaves);
+}
+
+// Writes into buf (NUL-terminated, at most len bytes) the kernel a call of
+// this shape launches on a device with ncu CUs, in the form profilers print
+// template instances ("name<8, true, 12>"), with its launch count and grid.
+// op: 0 moe_finalize, 1 moe_finalize_residual_rmsnorm, 2 moe_finalize_quant_ue8m0.
+void describe_finalize(int op, int64_t tokens, int64_t hidden, int top_k, int ncu, char* buf,
+                       int64_t len);
+
+// CUs of the device that runs `stream` (the current device for the null
+// stream), or 0 if the runtime cannot say.
+int device_cus(hipStream_t stream);
+
 // The RMSNorm epilogue with two column vectors per lane holds at most 20
 // waves per CU (5 per SIMD): measured faster at large T than the 24 its
 // register use would allow.

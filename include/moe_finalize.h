@@ -339,6 +339,34 @@ int moe_act_quant_fp8_ue8m0(const uint16_t* x, int64_t num_tokens, int64_t hidde
 int moe_act_quant_fp8_amax(const uint16_t* x, int64_t num_tokens, int64_t hidden,
                            uint8_t* out_e4m3, float* scale_f32, void* stream);
 
+/* Operations moe_finalize_describe_launch describes. */
+enum moef_op {
+  MOEF_OP_FINALIZE = 0,           /* moe_finalize */
+  MOEF_OP_RESIDUAL_RMSNORM = 1,   /* moe_finalize_residual_rmsnorm */
+  MOEF_OP_QUANT_UE8M0 = 2         /* moe_finalize_quant_ue8m0 */
+};
+
+/*
+ * moe_finalize_describe_launch - which kernel a finalize call of this shape
+ * launches on the device of `stream`, and how many launches of what grid.
+ * It computes nothing and launches nothing: benchmarks and profiles use it
+ * to name the kernel they time. (No page defines it; the kernels it names
+ * implement the operations above.)
+ *
+ *  op          a MOEF_OP_* value.
+ *  num_tokens, hidden, top_k  as the call's, under the same shape rules.
+ *  stream      its device's CU count sizes the staged (one workgroup per CU)
+ *              kernels; the count of each device is queried once and kept.
+ *  buf         receives one NUL-terminated line, cut to buf_len - 1 bytes:
+ *              the kernel as profilers print it, e.g.
+ *              "finalize_quant_staged_kernel<8, true, 12> launches=1
+ *              grid=616x1024 groups=8 tail=5%" (workgroups x lanes).
+ *  Errors: a NULL buf or buf_len < 1 gives NULL_POINTER; an unknown op gives
+ *  BAD_SHAPE; the call's shape rules give BAD_SHAPE or UNSUPPORTED.
+ */
+int moe_finalize_describe_launch(int32_t op, int64_t num_tokens, int64_t hidden, int32_t top_k,
+                                 void* stream, char* buf, int64_t buf_len);
+
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* moe_finalize_status_string(int status);
 

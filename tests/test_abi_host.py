@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
                           "moe_finalize_status_string", "moe_finalize_abi_version",
                           "moe_topk_sigmoid_gate", "moe_act_quant_fp8_ue8m0",
                           "moe_act_quant_fp8_amax", "moe_finalize_ep_combine",
-                          "moe_allreduce_residual_rmsnorm"}
+                          "moe_allreduce_residual_rmsnorm", "moe_finalize_describe_launch"}
     for n in names:
         assert hasattr(lib, n), n
 

@@ -2,11 +2,12 @@
 
 From 48 (token, chunk) units per CU the bf16 finalize runs one workgroup per
 CU that takes units from an LDS counter, keeps each unit's 1 KiB of output in
-LDS (159 units per CU) and, past that, in 8 register slots per wave, and
-writes it all after its last gather; grids larger than that take several
-launches. The grids here are sized from the device's CU count so that each
-case lands on one of those paths; every output is compared bit for bit with
-the oracle's fp32 mirror."""
+LDS (159 units per CU) and, past that, in register slots, and writes it all
+after its last gather. Workgroups of 16 waves with 8 slots a wave hold 287
+units per CU; larger grids take workgroups of 12 waves with 25 slots a wave
+(459 units per CU) and, past that, several launches. The grids here are
+sized from the device's CU count so that each case lands on one of those
+paths; every output is compared bit for bit with the oracle's fp32 mirror."""
 import numpy as np
 import pytest
 import torch
@@ -209,3 +210,41 @@ def test_random_staged_configs(ncu, case):
              f"packed={packed} shared={with_shared}")
     got = run_plain(wl, packed=packed, with_shared=with_shared, idx=idx)
     check_mirror(wl, got, packed=packed, with_shared=with_shared, idx=idx)
+
+
+def test_exactly_one_launch_capacity(ncu):
+    """H = 128 at the largest grid one launch holds: every workgroup gets
+    287 units, 159 in LDS and 16 x 8 in register slots, so a wave that takes
+    more than its share of the units past the LDS slots writes its extra
+    units at once."""
+    H, k = 128, 4
+    T = (LDS_UNITS + REG_UNITS_PER_CU) * ncu
+    wl = W.make_workload(T, H, 16, k, rsf=2.5, seed=815, pad=64)
+    announce(f"staged finalize at one launch's capacity T={T} H={H} k={k}")
+    got = run_plain(wl)
+    check_mirror(wl, got)
+
+
+WIDE_UNITS_PER_CU = 159 + 12 * 25
+
+
+def test_wide_layout_at_capacity(ncu):
+    """Past what one 16-wave launch holds, the plain finalize takes 12-wave
+    workgroups with 25 register slots a wave: H = 128 at exactly one such
+    launch's capacity (459 units per CU, 300 of them in register slots)."""
+    H, k = 128, 4
+    T = WIDE_UNITS_PER_CU * ncu
+    wl = W.make_workload(T, H, 16, k, rsf=2.5, seed=816, pad=64)
+    announce(f"staged finalize, wide layout at capacity T={T} H={H} k={k}")
+    got = run_plain(wl, packed=True)
+    check_mirror(wl, got, packed=True)
+
+
+def test_wide_layout_prefill_shape(ncu):
+    """The prefill shape the wide layout exists for (T = 8192, H = 7168,
+    top_k = 8: 448 units per CU on 256 CUs, one launch), against the mirror."""
+    wl = W.config_workload(4)
+    announce(f"staged finalize, prefill T={wl.T} H={wl.H} (wide layout from "
+             f"{(LDS_UNITS + REG_UNITS_PER_CU) * ncu} units)")
+    got = run_plain(wl)
+    check_mirror(wl, got, chunk=2048)

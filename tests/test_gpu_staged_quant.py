@@ -1,7 +1,8 @@
 """GPU parity of the UE8M0 finalize's staged-output path.
 
 From 80 (token, chunk) units per CU the quant finalize runs one workgroup per
-CU that takes units from an LDS counter, keeps their codes and scale bytes in
+CU (tokens dealt to one group of workgroups per XCD in blocks of 16) that
+takes units from an LDS counter, keeps their codes and scale bytes in
 LDS (317 units per CU) and, past that, in 12 register slots per wave, and
 writes them after its last gather; grids larger than that take several
 launches. These tests size their grids from the device's CU count so that
@@ -227,3 +228,18 @@ def test_random_staged_configs(ncu, case):
              f"packed={packed} shared={with_shared}")
     q, s = run_quant(wl, packed=packed, with_shared=with_shared, idx=idx)
     check_mirror(wl, q, s, packed=packed, with_shared=with_shared, idx=idx)
+
+
+def test_exactly_one_launch_capacity(ncu):
+    """H = 128 (one chunk per token) at the largest grid one launch holds:
+    every workgroup gets 509 units, 317 in LDS and 16 x 12 in register
+    slots, so a wave that takes more than its share of the units past the
+    LDS slots writes its extra units at once. The placement deals the tokens
+    to groups of workgroups (one group per XCD) in blocks of 16."""
+    H, k = 128, 2
+    T = (LDS_UNITS + REG_UNITS_PER_CU) * ncu
+    wl = W.make_workload(T, H, 16, k, rsf=2.5, seed=719, pad=64, log2_mag=(-8, 8))
+    announce(f"staged quant at one launch's capacity T={T} H={H} k={k}")
+    q, s = run_quant(wl)
+    check_mirror(wl, q, s)
+
