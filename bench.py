@@ -190,7 +190,9 @@ def e4m3_steps(a, b):
 
 
 def host_threads():
-    """Host CPUs this process may run on, at most 16 (one GPU's share of the host)."""
+    """Threads for the CPU leg: the host CPUs this process may run on, at most
+    16 (one GPU's share of its host: the 8-GPU hosts these numbers come from
+    give each GPU's jobs 16 CPUs, and the affinity mask can show more)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -198,32 +200,33 @@ def host_threads():
     return max(1, min(n, 16))
 
 
-def oracle_chunk(O, wl, sl):
-    return O.finalize_quant_truth(wl.gemm2_out, wl.idx[sl], weights_f32=wl.weights[sl],
-                                  shared=wl.shared[sl], rsf=wl.rsf)
+def oracle_chunk(O, wl, sl, mode="mirror"):
+    fn = O.finalize_quant_mirror if mode == "mirror" else O.finalize_quant_truth
+    return fn(wl.gemm2_out, wl.idx[sl], weights_f32=wl.weights[sl], shared=wl.shared[sl],
+              rsf=wl.rsf)
 
 
 def cpu_baseline(wl, q_gpu=None, s_gpu=None, min_s=10.0, max_s=30.0, chunk=256,
-                 mirror_tokens=512, threads=None, min_s_threads=5.0):
-    """The oracle (fp64 truth finalize + UE8M0 quant), as it stands, in token
-    chunks over the same workload.
+                 truth_tokens=512, threads=None, min_s_threads=5.0):
+    """The oracle's fp32 mirror of the kernels' operation order (finalize +
+    UE8M0 quant, numpy), as it stands, in token chunks over the same
+    workload: the CPU counterpart of the timed launch.
 
     One thread first, repeating passes until at least min_s seconds of CPU
-    work (stopping early at max_s); then, with threads > 1 (default: the
-    host CPUs available, at most 16), the same chunks spread over a thread
-    pool for at least min_s_threads seconds. The reported value is the
-    thread-pool rate (cores = its thread count), the one-thread rate beside it.
+    work (stopping early at max_s); then, with threads > 1 (default: the host
+    CPUs available, at most 16), the same chunks on a thread pool for at
+    least min_s_threads seconds. The reported value is the thread-pool rate
+    (cores = its thread count), the one-thread rate beside it.
 
-    With the GPU's codes and scale bytes given, the first one-thread pass's
-    oracle outputs are also compared with them after the timing: against the
-    fp64 truth over every token (scale bytes equal, codes within one step),
-    and against the oracle's fp32 mirror of the kernels' operation order,
-    untimed, on the first mirror_tokens tokens (bit-exact)."""
+    With the GPU's codes and scale bytes given, they are then compared with
+    the first one-thread pass's outputs (bit for bit, every token it
+    covered), and, untimed, with the oracle's fp64 truth on the first
+    truth_tokens tokens (scale bytes equal, codes within one E4M3 step)."""
     from concurrent.futures import ThreadPoolExecutor
     from oracle import finalize as O
     keep = q_gpu is not None
-    t_codes = np.empty((wl.T, wl.H), np.uint8) if keep else None
-    t_scales = np.empty((wl.T, wl.H // 128), np.uint8) if keep else None
+    m_codes = np.empty((wl.T, wl.H), np.uint8) if keep else None
+    m_scales = np.empty((wl.T, wl.H // 128), np.uint8) if keep else None
     done = 0
     t0 = time.perf_counter()
     while True:
@@ -231,7 +234,7 @@ def cpu_baseline(wl, q_gpu=None, s_gpu=None, min_s=10.0, max_s=30.0, chunk=256,
         sl = slice(start, min(wl.T, start + chunk))
         qc, sc, _ = oracle_chunk(O, wl, sl)
         if keep and done < wl.T:
-            t_codes[sl], t_scales[sl] = qc, sc
+            m_codes[sl], m_scales[sl] = qc, sc
         done += sl.stop - sl.start
         el = time.perf_counter() - t0
         if (el >= min_s and done % wl.T == 0) or el >= max_s:
@@ -242,9 +245,9 @@ def cpu_baseline(wl, q_gpu=None, s_gpu=None, min_s=10.0, max_s=30.0, chunk=256,
            "sample": f"{done} tokens ({done / wl.T:.2f} passes over the T={wl.T} workload), "
                      f"{dt:.1f} s"}
     n_thr = host_threads() if threads is None else threads
+    what = "the oracle's fp32 mirror of the finalize + UE8M0/E4M3 quant, numpy"
     base = {"value": round(gbs1, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{one['sample']} through the fp64 finalize + UE8M0/E4M3 quant oracle, "
-                      f"numpy, one thread"}
+            "sample": f"{one['sample']} through {what}, one thread"}
     if n_thr > 1:
         slices = [slice(a, min(wl.T, a + chunk)) for a in range(0, wl.T, chunk)]
         mt_done, passes = 0, 0
@@ -261,78 +264,122 @@ def cpu_baseline(wl, q_gpu=None, s_gpu=None, min_s=10.0, max_s=30.0, chunk=256,
         base = {"value": round(bytes_quant(mt_done, wl.H, wl.top_k) / dt_mt / 1e9, 4),
                 "unit": "GB/s", "cores": n_thr, "kind": "oracle",
                 "sample": f"{mt_done} tokens ({passes} passes over the T={wl.T} workload) "
-                          f"through the fp64 finalize + UE8M0/E4M3 quant oracle, numpy, "
-                          f"{n_thr} threads over {chunk}-token chunks, {dt_mt:.1f} s",
+                          f"through {what}, {n_thr} threads over {chunk}-token chunks, "
+                          f"{dt_mt:.1f} s",
                 "single_thread": one}
     if not keep:
         return base, None
     n = min(done, wl.T)
-    steps = e4m3_steps(q_gpu[:n], t_codes[:n])
-    m = min(mirror_tokens, wl.T)
-    mq, ms, _ = O.finalize_quant_mirror(wl.gemm2_out, wl.idx[:m], weights_f32=wl.weights[:m],
-                                        shared=wl.shared[:m], rsf=wl.rsf)
-    parity = {"tokens_vs_fp64_truth": int(n),
-              "scale_bytes_differing_vs_truth": int(np.count_nonzero(s_gpu[:n] != t_scales[:n])),
+    m = min(truth_tokens, wl.T)
+    tq, ts, _ = O.finalize_quant_truth(wl.gemm2_out, wl.idx[:m], weights_f32=wl.weights[:m],
+                                       shared=wl.shared[:m], rsf=wl.rsf)
+    steps = e4m3_steps(q_gpu[:m], tq)
+    parity = {"tokens_vs_fp32_mirror": int(n),
+              "code_mismatches_vs_mirror": int(np.count_nonzero(q_gpu[:n] != m_codes[:n])),
+              "scale_mismatches_vs_mirror": int(np.count_nonzero(s_gpu[:n] != m_scales[:n])),
+              "tokens_vs_fp64_truth": int(m),
+              "scale_bytes_differing_vs_truth": int(np.count_nonzero(s_gpu[:m] != ts)),
               "max_code_steps_vs_truth": int(steps.max()) if steps.size else 0,
-              "codes_differing_vs_truth": int(np.count_nonzero(steps)),
-              "tokens_vs_fp32_mirror": int(m),
-              "code_mismatches_vs_mirror": int(np.count_nonzero(q_gpu[:m] != mq)),
-              "scale_mismatches_vs_mirror": int(np.count_nonzero(s_gpu[:m] != ms))}
+              "codes_differing_vs_truth": int(np.count_nonzero(steps))}
     return base, parity
 
 
 # ----------------------------------------------------------------- sweep
+def probe_lib():
+    """The bandwidth probe library (csrc/bandwidth_probes.h); fails loudly
+    when it is not built."""
+    import ctypes
+    from combine_moe_finalize_amd._paths import PROBE_LIB_PATH
+    P = ctypes.CDLL(PROBE_LIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    P.moef_probe_read.argtypes = [vp, i64, vp, vp]
+    P.moef_probe_copy.argtypes = [vp, vp, i64, vp]
+    P.moef_probe_empty.argtypes = [vp]
+    P.moef_probe_mark.argtypes = [vp]
+    return P
+
+
 def sweep(torch, M, W, iters_small=200, iters_big=50):
-    flush_buf = torch.empty(1 << 29, dtype=torch.int16, device="cuda:0")   # 1 GiB
+    """Every workload shape and NEXT-row entry point. Before each case the
+    probe library's marker kernel (the empty kernel on two workgroups) is
+    launched, so a kernel trace of this run splits into one block per case,
+    in the order of the returned rows. A case's dispatches: 5 warm-up calls,
+    `iters` back-to-back event-timed calls (warm), iters / 10 calls each
+    after a 1 GiB read-only stream through the caches (cold), 100
+    back-to-back calls, and 20 calls captured in a HIP graph and replayed.
+    The read-only flush leaves no dirty lines behind, so a cold call is not
+    charged for writing back someone else's data."""
+    P = probe_lib()
+    flush_src = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda:0")
+    flush_sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+
+    def stream():
+        return torch.cuda.current_stream().cuda_stream
 
     def flush():
-        flush_buf.fill_(1)
+        if P.moef_probe_read(flush_src.data_ptr(), 1 << 30, flush_sink.data_ptr(), stream()) != 0:
+            raise RuntimeError("read probe: launch failed")
 
     rows = []
 
-    def measure(name, T, H, k, nbytes, fn, iters):
+    def measure(name, T, H, k, nbytes, fn, iters, kernel=None):
+        torch.cuda.synchronize()
+        if P.moef_probe_mark(stream()) != 0:
+            raise RuntimeError("marker launch failed")
+        torch.cuda.synchronize()
         for _ in range(5):
             fn()
         warm = event_times_us(torch, fn, iters)
         cold = event_times_us(torch, fn, max(10, iters // 10), flush=flush)
         batched = batched_us(torch, fn, 100)
         graph = graph_us(torch, fn, 20)
-        rows.append({"case": name, "T": T, "H": H, "top_k": k,
-                     "us_event_median": round(float(np.median(warm)), 3),
-                     "us_event_p10": round(float(np.percentile(warm, 10)), 3),
-                     "us_event_p90": round(float(np.percentile(warm, 90)), 3),
-                     "us_event_cold_median": round(float(np.median(cold)), 3),
-                     "us_batched": round(batched, 3),
+        rows.append({"case": name, "T": T, "H": H, "top_k": k, "kernel": kernel,
                      "us_graph_replay": round(graph, 3),
-                     "gbs_batched": round(nbytes / (batched * 1e-6) / 1e9, 1),
-                     "gbs_event_cold": round(nbytes / (np.median(cold) * 1e-6) / 1e9, 1),
-                     "algorithmic_bytes": int(nbytes)})
+                     "gbs_graph_replay": round(nbytes / (graph * 1e-6) / 1e9, 1),
+                     "algorithmic_bytes": int(nbytes),
+                     # per-call times seen from the host: each includes the launch and
+                     # event overhead (several us at decode sizes); kernel-only times,
+                     # warm and cold, come from the kernel trace of this run
+                     "host_inclusive": {
+                         "us_event_median": round(float(np.median(warm)), 3),
+                         "us_event_p10": round(float(np.percentile(warm, 10)), 3),
+                         "us_event_p90": round(float(np.percentile(warm, 90)), 3),
+                         "us_event_cold_median": round(float(np.median(cold)), 3),
+                         "us_batched": round(batched, 3)}})
         log(f"sweep {rows[-1]}")
 
+    def describe(op, T, H, k):
+        return M.moe_finalize_describe_launch(op, T, H, k)
+
+    measure("empty kernel (launch floor)", 0, 0, 0, 0, lambda: P.moef_probe_empty(stream()),
+            iters_small, kernel="empty_probe_kernel")
     wl = W.config_workload(0)
     kw, _ = upload(wl, torch)
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
     measure("tiny", wl.T, wl.H, wl.top_k, bytes_plain(wl.T, wl.H, wl.top_k),
-            lambda: M.moe_finalize(**kw, out=out), iters_small)
+            lambda: M.moe_finalize(**kw, out=out), iters_small,
+            kernel=describe(M.OP_FINALIZE, wl.T, wl.H, wl.top_k))
     for T in W.CONFIGS[1]["Ts"]:
         wl = W.config_workload(1, T)
         kw, _ = upload(wl, torch)
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
         measure("decode", T, wl.H, wl.top_k, bytes_plain(T, wl.H, wl.top_k),
-                lambda: M.moe_finalize(**kw, out=out), iters_small)
+                lambda: M.moe_finalize(**kw, out=out), iters_small,
+                kernel=describe(M.OP_FINALIZE, T, wl.H, wl.top_k))
     for T in (1, 16):                      # the Kimi K2.5 decode shape (H 7168, 384 experts)
         wl = W.make_workload(T, 7168, 384, 8, rsf=2.5, seed=W.default_seed(9, T))
         kw, _ = upload(wl, torch)
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
         measure("decode_H7168_E384", T, wl.H, wl.top_k, bytes_plain(T, wl.H, wl.top_k),
-                lambda: M.moe_finalize(**kw, out=out), iters_small)
+                lambda: M.moe_finalize(**kw, out=out), iters_small,
+                kernel=describe(M.OP_FINALIZE, T, wl.H, wl.top_k))
     wl = W.config_workload(2)
     for packed in (False, True):
         kw, _ = upload(wl, torch, packed=packed)
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
         measure("packed" if packed else "fp32_weights", wl.T, wl.H, wl.top_k,
                 bytes_plain(wl.T, wl.H, wl.top_k), lambda: M.moe_finalize(**kw, out=out),
-                iters_small)
+                iters_small, kernel=describe(M.OP_FINALIZE, wl.T, wl.H, wl.top_k))
     for T in W.CONFIGS[3]["Ts"]:
         wl = W.config_workload(3, T)
         kw, ex = upload(wl, torch)
@@ -340,7 +387,8 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
         nm = torch.empty_like(ro)
         measure("residual_rmsnorm", T, wl.H, wl.top_k, bytes_rmsnorm(T, wl.H, wl.top_k),
                 lambda: M.moe_finalize_residual_rmsnorm(**kw, **ex, residual_out=ro, normed=nm),
-                iters_big if T >= 1024 else iters_small)
+                iters_big if T >= 1024 else iters_small,
+                kernel=describe(M.OP_RESIDUAL_RMSNORM, T, wl.H, wl.top_k))
     for T in (1, 256, 8192):
         E, k = 256, 8
         lg = torch.from_numpy(W.router_logits(T, E, seed=T)).to("cuda:0")
@@ -390,7 +438,7 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
     wts = torch.empty(pk.shape, dtype=torch.float32, device="cuda:0")
     measure("packed_decode", 8192, 0, 8, 12 * n,
             lambda: M.moe_topk_packed_decode(pk, expert_ids=ids, weights=wts), iters_small)
-    del flush_buf
+    del flush_src, flush_sink
     torch.cuda.empty_cache()
     return rows
 
@@ -399,10 +447,7 @@ def launch_floor_us(torch):
     """Per-call time of the probe library's empty kernel (one wave, no memory
     access) under the same HIP-graph replay as the small calls: the floor
     under any kernel's time per call."""
-    import ctypes
-    from combine_moe_finalize_amd._paths import PROBE_LIB_PATH
-    P = ctypes.CDLL(PROBE_LIB_PATH)                  # fails loudly when it is not built
-    P.moef_probe_empty.argtypes = [ctypes.c_void_p]
+    P = probe_lib()
 
     def launch():
         if P.moef_probe_empty(torch.cuda.current_stream().cuda_stream) != 0:
@@ -413,15 +458,10 @@ def launch_floor_us(torch):
 
 def ceilings(torch, nbytes=1 << 30):
     """Same-session HBM rates in GB/s: the streaming read and copy probes
-    (moe_bandwidth_probes.h) over `nbytes`, 10 back-to-back launches between
+    (csrc/bandwidth_probes.h) over `nbytes`, 10 back-to-back launches between
     two events, median of 5; and torch's own device-to-device copy, median
     of 20 event-timed copies. A copy moves 2 x nbytes."""
-    import ctypes
-    from combine_moe_finalize_amd._paths import PROBE_LIB_PATH
-    P = ctypes.CDLL(PROBE_LIB_PATH)                  # fails loudly when it is not built
-    vp, i64 = ctypes.c_void_p, ctypes.c_int64
-    P.moef_probe_read.argtypes = [vp, i64, vp, vp]
-    P.moef_probe_copy.argtypes = [vp, vp, i64, vp]
+    P = probe_lib()
     src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
     sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
@@ -464,6 +504,211 @@ def ceilings(torch, nbytes=1 << 30):
     return read, copy, torch_copy
 
 
+# ------------------------------------------------------- profile summaries
+# CPU-only: these read what rocprofv3 wrote during a run of this script and
+# write the summaries kept under profiles/.
+
+def _short_kernel(name):
+    """A trace's kernel name without namespaces and arguments:
+    "finalize_quant_staged_kernel<8, true, 12>"."""
+    import re
+    core = name.replace("(anonymous namespace)::", "").split("(", 1)[0]
+    core = core.replace("void ", "", 1).strip() if core.startswith("void ") else core.strip()
+    depth, cut = 0, 0
+    for i, ch in enumerate(core):       # the last "::" outside template brackets
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == ":" and depth == 0 and i > 0 and core[i - 1] == ":":
+            cut = i + 1
+    out = core[cut:]
+    return re.sub(r"\s+", " ", out)
+
+
+def _read_trace(path):
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append({"name": _short_kernel(r["Kernel_Name"]), "grid": int(r["Grid_Size_X"]),
+                         "wg": int(r["Workgroup_Size_X"]), "id": int(r["Dispatch_Id"]),
+                         "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+    rows.sort(key=lambda r: r["id"])
+    return rows
+
+
+def _last_json_line(path):
+    with open(path) as f:
+        lines = [l for l in f.read().splitlines() if l.startswith("{")]
+    return json.loads(lines[-1])
+
+
+def _stats(us):
+    us = np.asarray(us, dtype=float)
+    if us.size == 0:
+        return None
+    return {"n": int(us.size), "median": float(np.median(us)), "p10": float(np.percentile(us, 10)),
+            "p90": float(np.percentile(us, 90))}
+
+
+def summarize_trace(trace_csv, bench_json, out_dir, command):
+    """The kernel trace of one `bench.py` run: the timed launches of the
+    headline call, and per sweep case the kernel's durations split into warm
+    dispatches and cold ones (those right after the 1 GiB read-only flush)."""
+    rows = _read_trace(trace_csv)
+    line = _last_json_line(bench_json)
+    srcs = kernel_source_hash()
+    # headline: the first warmup + steps dispatches of the timed kernel
+    kname = line["roofline"]["kernel"].split(" launches=")[0]
+    grid = line["roofline"]["kernel"].split(" grid=")[1].split()[0]
+    nwg, wg = (int(x) for x in grid.split("x"))
+    nhead = line["warmup"] + line["steps"]
+    head = [r for r in rows if r["name"] == kname and r["grid"] == nwg * wg][:nhead]
+    timed = [r["us"] for r in head[line["warmup"]:]]
+    nbytes = line["roofline"]["algorithmic_bytes_per_launch"]
+    hl = [f"# {kname}: prefill FP8/UE8M0 finalize, T={line['config']['tokens']}, "
+          f"H={line['config']['hidden']}, top_k={line['config']['top_k']}", "",
+          "Command (from `/tmp` with `TMPDIR=/tmp` on the MI355X box; `$R` is the repository root):",
+          "", f"    {command}", "",
+          "Summary written by `python bench.py --summarize-trace` from that run's kernel trace "
+          "and JSON line.", "",
+          f"Kernel source SHA-256 (`finalize_kernels.hip` + `device_common.h` + "
+          f"`moef_internal.h`): `{srcs}`", "",
+          f"Launch, as `moe_finalize_describe_launch` reports it: `{line['roofline']['kernel']}`.",
+          "", "| dispatches | avg µs | median µs | min µs | max µs |", "|---|---|---|---|---|"]
+    avg = float(np.mean(timed)) if timed else float("nan")
+    hl.append(f"| {len(timed)} timed (after {line['warmup']} warm-up) | {avg:.3f} | "
+              f"{np.median(timed):.3f} | {min(timed):.3f} | {max(timed):.3f} |")
+    hl += ["", f"Algorithmic bytes per launch: {nbytes:,} → **{nbytes / avg / 1e3:,.0f} GB/s** at "
+           f"the timed average ({nbytes / avg / 1e3 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s).", "",
+           f"The same run's bench line (HIP events on the launch stream around the {line['steps']} "
+           f"timed launches): **{line['roofline']['kernel_us_avg']:.3f} µs** per launch "
+           f"({(line['roofline']['kernel_us_avg'] / avg - 1) * 100:+.1f}% against the trace).", ""]
+    with open(os.path.join(out_dir, "prefill_quant_T8192_H7168_kernel_trace.md"), "w") as f:
+        f.write("\n".join(hl))
+    # sweep: blocks between marker dispatches, in the order of the sweep rows
+    blocks, cur = [], None
+    for r in rows:
+        if r["name"] == "empty_probe_kernel" and r["grid"] == 128:
+            cur = []
+            blocks.append(cur)
+        elif cur is not None:
+            cur.append(r)
+    sw = line.get("sweep", [])
+    out = ["# Kernel durations of every bench sweep case (rocprofv3 kernel trace)", "",
+           "Same run and command as `prefill_quant_T8192_H7168_kernel_trace.md`:", "",
+           f"    {command}", "",
+           "Written by `python bench.py --summarize-trace`. Each sweep case starts with a marker "
+           "launch; its dispatches are 5 warm-up calls, back-to-back calls, calls each after a "
+           "1 GiB read-only stream through the caches (**cold**: the dispatch right after the "
+           "flush kernel), 100 back-to-back calls and 20-call HIP-graph replays. **Warm** is "
+           "every dispatch of the case's kernel that does not follow a flush. The first row, the "
+           "empty kernel (one wave, no memory access), is the floor under every other row, in "
+           "the same two states.", "",
+           f"Kernel source SHA-256 (`finalize_kernels.hip` + `device_common.h` + "
+           f"`moef_internal.h`): `{srcs}`", "",
+           "| case | kernel | grid | warm n | warm median µs | p10 | p90 | cold n | cold median µs "
+           "| algorithmic bytes | GB/s warm | GB/s cold |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    summary = []
+    for case, blk in zip(sw, blocks):
+        by = {}
+        for r in blk:
+            if r["name"] in ("read_probe_kernel",):
+                continue
+            by.setdefault((r["name"], r["grid"]), []).append(r)
+        if not by:
+            continue
+        key = max(by, key=lambda kk: sum(x["us"] for x in by[kk]))
+        ids = {r["id"] for r in by[key]}
+        warm, cold = [], []
+        prev = None
+        for r in blk:
+            if r["id"] in ids:
+                (cold if prev is not None and prev["name"] == "read_probe_kernel" else warm).append(r["us"])
+            prev = r
+        w, c = _stats(warm), _stats(cold)
+        nb = case["algorithmic_bytes"]
+        label = f"{case['case']} T={case['T']} H={case['H']} k={case['top_k']}"
+        gw = f"{nb / w['median'] / 1e3:,.1f}" if nb and w else "—"
+        gc = f"{nb / c['median'] / 1e3:,.1f}" if nb and c else "—"
+        out.append(f"| {label} | `{key[0]}` | {key[1]} | {w['n']} | {w['median']:.3f} | "
+                   f"{w['p10']:.3f} | {w['p90']:.3f} | {c['n'] if c else 0} | "
+                   f"{c['median'] if c else float('nan'):.3f} | {nb:,} | {gw} | {gc} |")
+        summary.append({"case": label, "kernel": key[0], "grid": key[1], "warm": w, "cold": c,
+                        "algorithmic_bytes": nb})
+    with open(os.path.join(out_dir, "finalize_sweep_kernel_trace.md"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    return summary
+
+
+def summarize_counters(fetch_csv, write_csv, out_dir, commands):
+    """The two counter passes of `bench.py --copy-calibration --no-sweep`:
+    FETCH_SIZE and WRITE_SIZE of the three 1 GiB device copies (the factor
+    that turns each counter into bytes) and of the headline launches."""
+    import csv
+
+    def read(path, counter):
+        d = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = int(r["Dispatch_Id"])
+                e = d.setdefault(k, {"name": _short_kernel(r["Kernel_Name"]), "v": 0.0})
+                if r["Counter_Name"] == counter:
+                    e["v"] += float(r["Counter_Value"])
+        return [d[k] for k in sorted(d)]
+
+    fe, wr = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
+    cf = [r["v"] for r in fe if r["name"] == "__amd_rocclr_copyBuffer"][:3]
+    cw = [r["v"] for r in wr if r["name"] == "__amd_rocclr_copyBuffer"][:3]
+    qf = [r["v"] for r in fe if r["name"].startswith("finalize_quant")]
+    qw = [r["v"] for r in wr if r["name"].startswith("finalize_quant")]
+    qname = next(r["name"] for r in fe if r["name"].startswith("finalize_quant"))
+    ff, fw = (1 << 30) / (np.median(cf) * 1024), (1 << 30) / (np.median(cw) * 1024)
+    fk, wk = float(np.median(qf[1:])), float(np.median(qw[1:]))     # the first is the warm-up
+    fb, wb = fk * 1024 * ff, wk * 1024 * fw
+    nbytes = bytes_quant(8192, 7168, 8)
+    reads = 8192 * (2 * 7168 * 9 + 64)
+    j = {"kernel": qname,
+         "workload": "prefill finalize + UE8M0/E4M3, T=8192, H=7168, E=256, top_k=8, fp32 "
+                     "weights, shared expert",
+         "kernel_source_sha256": kernel_source_hash(),
+         "fetch_size_kib_per_launch": fk, "write_size_kib_per_launch": wk,
+         "copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                              "fetch_size_kib": float(np.median(cf)),
+                              "write_size_kib": float(np.median(cw)),
+                              "fetch_factor": round(float(ff), 6), "write_factor": round(float(fw), 6)},
+         "fetch_bytes_per_launch": int(round(fb)), "write_bytes_per_launch": int(round(wb)),
+         "hbm_bytes_per_launch": int(round(fb + wb)), "algorithmic_bytes_per_launch": nbytes,
+         "traffic_over_algorithmic": round((fb + wb) / nbytes, 5)}
+    with open(os.path.join(out_dir, "prefill_quant_T8192_H7168_counters.json"), "w") as f:
+        json.dump(j, f, indent=1)
+    md = [f"# HBM traffic counters: {qname}, prefill T=8192, H=7168, top_k=8", "",
+          "Two counter passes, each in its own run (from `/tmp` with `TMPDIR=/tmp` on the MI355X "
+          "box; `$R` is the repository root there):", ""]
+    md += [f"    {c}" for c in commands]
+    md += ["", "`--copy-calibration` adds three 1 GiB device-to-device copies "
+           "(`__amd_rocclr_copyBuffer`) that read and write exactly 1 073 741 824 bytes each. "
+           "Written by `python bench.py --summarize-counters`.", "",
+           f"Kernel source SHA-256: `{j['kernel_source_sha256']}`", "",
+           "| dispatch | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|",
+           "| copy 1 GiB (×3) | " + " / ".join(f"{v:,.1f}" for v in cf) + " | "
+           + " / ".join(f"{v:,.1f}" for v in cw) + " |",
+           f"| {qname} (×{len(qf)}: 1 warm-up + {len(qf) - 1}) | "
+           + " / ".join(f"{v:,.1f}" for v in qf) + " | " + " / ".join(f"{v:,.1f}" for v in qw) + " |",
+           "", f"Calibration (known bytes / counter reading): fetch {ff:.6f}, write {fw:.6f}.", "",
+           f"Per launch (median of the timed launches): fetch {fk:,.1f} KiB × {ff:.6f} = "
+           f"{int(round(fb)):,} B; write {wk:,.1f} KiB × {fw:.6f} = {int(round(wb)):,} B; "
+           f"**total {int(round(fb + wb)):,} B** against {nbytes:,} algorithmic bytes "
+           f"(**{(fb + wb) / nbytes:.4f}×**). Reads: {fb / reads:.4f}× the algorithmic "
+           f"{reads:,} B; writes: {wb / (nbytes - reads):.4f}× the algorithmic "
+           f"{nbytes - reads:,} B.", ""]
+    with open(os.path.join(out_dir, "prefill_quant_T8192_H7168_counters.md"), "w") as f:
+        f.write("\n".join(md))
+    return j
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -475,7 +720,22 @@ def main():
                     help="skip the shape sweep, the T curve and the same-session ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"),
+                    help="CPU only: write the kernel-trace summaries under profiles/ from a "
+                         "rocprofv3 kernel trace of this script and its JSON line")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="CPU only: write the counter summary under profiles/ from the "
+                         "FETCH_SIZE and WRITE_SIZE passes")
+    ap.add_argument("--command", action="append", default=[],
+                    help="the command that made the summarized data (recorded verbatim)")
     args = ap.parse_args()
+    out_dir = os.path.join(ROOT, "profiles")
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, out_dir, " ".join(args.command) or "(not given)")
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, out_dir, args.command or ["(not given)"])
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the finalize "
@@ -505,6 +765,10 @@ def main():
 
     def step():
         M.moe_finalize_quant_ue8m0(**kw, out_e4m3=q, scale_e8m0=s)
+
+    # the kernel this call launches on this device, as the library plans it
+    kernel = M.moe_finalize_describe_launch(M.OP_QUANT_UE8M0, T, H, k)
+    log(f"timed call: {kernel}")
 
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda:0").fill_(3)
@@ -547,17 +811,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "prefill_finalize_fp8_ue8m0", "tokens": T, "hidden": H,
                    "experts": wl.E, "top_k": k, "padded_rows": wl.P,
                    "routed_scaling_factor": wl.rsf, "shared_expert": True,
-                   "routing": "fp32 weights", "io": "bf16 in, e4m3 + ue8m0 out",
+                   "routing": "fp32 weights",
+                   "io": "bf16 in, fp32 accumulation, e4m3 + ue8m0 out",
                    "algorithmic_bytes_per_step": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": counters_traffic(),
-                     "kernel": "finalize_quant_staged_kernel<8,true,12>",
+                     "kernel": kernel,
                      "kernel_us_avg": round(avg_us, 3),
                      "kernel_us_method": f"HIP events on the launch stream around the {args.steps} "
                                          f"timed launches, divided by {args.steps}",
@@ -571,7 +836,7 @@ def main():
             "read_gbs": round(read_gbs, 1), "copy_gbs": round(copy_gbs, 1),
             "torch_copy_gbs": round(torch_copy_gbs, 1),
             "method": "1 GiB streams after the timed launches: the read and copy probes "
-                      "(moe_bandwidth_probes.h), 10 launches per event pair, median of 5; "
+                      "(csrc/bandwidth_probes.h), 10 launches per event pair, median of 5; "
                       "torch's device copy, median of 20",
             "headline_frac_of_read": round(achieved / read_gbs, 4),
             "headline_frac_of_copy": round(achieved / copy_gbs, 4)}

@@ -64,7 +64,7 @@ def build_probes() -> str:
     tmp = PROBE_LIB_PATH + ".tmp"
     cmd = [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall",
-           "-I", INCLUDE, os.path.join(CSRC, "bandwidth_probes.hip"), "-o", tmp]
+           "-I", CSRC, os.path.join(CSRC, "bandwidth_probes.hip"), "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stderr}")

@@ -1,5 +1,5 @@
 /*
- * moe_bandwidth_probes.h - streaming read and copy kernels that measure the
+ * bandwidth_probes.h - streaming read and copy kernels that measure the
  * HBM rates one MI355X reaches in the same session as a benchmark, so the
  * finalize kernels can be reported against a measured ceiling beside the
  * 8 TB/s specification, and an empty kernel for the per-launch floor.
@@ -23,8 +23,8 @@
  * dst not 16-byte aligned, sink not 4-byte aligned), 6 (dst overlaps src),
  * 7 (the HIP runtime rejected the launch). Checks run before any HIP call.
  */
-#ifndef MOE_BANDWIDTH_PROBES_H
-#define MOE_BANDWIDTH_PROBES_H
+#ifndef MOEF_BANDWIDTH_PROBES_H
+#define MOEF_BANDWIDTH_PROBES_H
 
 #include <stdint.h>
 
@@ -45,8 +45,13 @@ int moef_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
  * floor under any kernel's time per call. Returns 0, or 7. */
 int moef_probe_empty(void* stream);
 
+/* The same empty kernel on two workgroups: a marker a benchmark launches
+ * between the cases it times, so that a kernel trace splits into one block
+ * per case (its grid tells it apart from moef_probe_empty). Returns 0, or 7. */
+int moef_probe_mark(void* stream);
+
 #ifdef __cplusplus
 }
 #endif
 
-#endif /* MOE_BANDWIDTH_PROBES_H */
+#endif /* MOEF_BANDWIDTH_PROBES_H */

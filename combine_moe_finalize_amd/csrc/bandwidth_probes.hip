@@ -12,7 +12,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "moe_bandwidth_probes.h"
+#include "bandwidth_probes.h"
 
 namespace {
 
@@ -86,6 +86,11 @@ int moef_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
 
 int moef_probe_empty(void* stream) {
   hipLaunchKernelGGL(empty_probe_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
+int moef_probe_mark(void* stream) {
+  hipLaunchKernelGGL(empty_probe_kernel, dim3(2), dim3(64), 0, static_cast<hipStream_t>(stream));
   return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 

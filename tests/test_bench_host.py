@@ -94,21 +94,23 @@ def test_committed_counters_match_the_committed_source():
 
 
 def test_parity_statistics_of_the_cpu_leg():
-    """The CPU leg's parity report: outputs equal to the oracle's fp32 mirror
-    show no mismatch; one flipped code is counted against both references."""
+    """The CPU leg times the oracle's fp32 mirror and reports parity: outputs
+    equal to the mirror show no mismatch against it (every token of the
+    timed pass) and at most one step against the fp64 truth (its sample);
+    one flipped code is counted against both references."""
     from oracle import finalize as O
     wl = W.make_workload(40, 1024, 16, 8, rsf=2.5, seed=3, log2_mag=(-8.0, 8.0))
     q, s, _ = O.finalize_quant_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
                                       shared=wl.shared, rsf=wl.rsf)
-    base, par = bench.cpu_baseline(wl, q, s, min_s=0.0, max_s=60.0, chunk=16, mirror_tokens=24,
+    base, par = bench.cpu_baseline(wl, q, s, min_s=0.0, max_s=60.0, chunk=16, truth_tokens=24,
                                    threads=1)
-    assert base["kind"] == "oracle" and base["cores"] == 1
-    assert par["tokens_vs_fp64_truth"] == 40 and par["tokens_vs_fp32_mirror"] == 24
+    assert base["kind"] == "oracle" and base["cores"] == 1 and "fp32 mirror" in base["sample"]
+    assert par["tokens_vs_fp32_mirror"] == 40 and par["tokens_vs_fp64_truth"] == 24
     assert par["code_mismatches_vs_mirror"] == 0 and par["scale_mismatches_vs_mirror"] == 0
     assert par["max_code_steps_vs_truth"] <= 1
     q2 = q.copy()
     q2[3, 5] = q2[3, 5] ^ 0x04                     # four steps away
-    _, par2 = bench.cpu_baseline(wl, q2, s, min_s=0.0, max_s=60.0, chunk=16, mirror_tokens=24,
+    _, par2 = bench.cpu_baseline(wl, q2, s, min_s=0.0, max_s=60.0, chunk=16, truth_tokens=24,
                                  threads=1)
     assert par2["code_mismatches_vs_mirror"] == 1
     assert par2["max_code_steps_vs_truth"] >= 3

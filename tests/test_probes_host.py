@@ -7,7 +7,7 @@ import re
 
 import pytest
 
-from combine_moe_finalize_amd._paths import INCLUDE, PROBE_LIB_PATH
+from combine_moe_finalize_amd._paths import CSRC, PROBE_LIB_PATH
 
 GRAIN = 16384
 A, B = 0x10_0000_0000, 0x20_0000_0000      # fake device addresses, 256-byte aligned
@@ -25,10 +25,10 @@ def lib():
 
 
 def test_exports_the_header(lib):
-    text = open(os.path.join(INCLUDE, "moe_bandwidth_probes.h")).read()
+    text = open(os.path.join(CSRC, "bandwidth_probes.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = set(re.findall(r"^int\s+(\w+)\s*\(", text, flags=re.M))
-    assert names == {"moef_probe_read", "moef_probe_copy", "moef_probe_empty"}
+    assert names == {"moef_probe_read", "moef_probe_copy", "moef_probe_empty", "moef_probe_mark"}
     for n in names:
         assert hasattr(lib, n)
     assert re.search(r"#define MOEF_PROBE_GRAIN 16384", text)
