@@ -322,7 +322,7 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
 
     rows = []
 
-    def measure(name, T, H, k, nbytes, fn, iters, kernel=None):
+    def measure(name, T, H, k, nbytes, fn, iters, kernel=None, write_bytes=None):
         torch.cuda.synchronize()
         if P.moef_probe_mark(stream()) != 0:
             raise RuntimeError("marker launch failed")
@@ -337,6 +337,7 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
                      "us_graph_replay": round(graph, 3),
                      "gbs_graph_replay": round(nbytes / (graph * 1e-6) / 1e9, 1),
                      "algorithmic_bytes": int(nbytes),
+                     "algorithmic_write_bytes": None if write_bytes is None else int(write_bytes),
                      # per-call times seen from the host: each includes the launch and
                      # event overhead (several us at decode sizes); kernel-only times,
                      # warm and cold, come from the kernel trace of this run
@@ -352,34 +353,35 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
         return M.moe_finalize_describe_launch(op, T, H, k)
 
     measure("empty kernel (launch floor)", 0, 0, 0, 0, lambda: P.moef_probe_empty(stream()),
-            iters_small, kernel="empty_probe_kernel")
+            iters_small, kernel="empty_probe_kernel", write_bytes=0)
     wl = W.config_workload(0)
     kw, _ = upload(wl, torch)
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
     measure("tiny", wl.T, wl.H, wl.top_k, bytes_plain(wl.T, wl.H, wl.top_k),
             lambda: M.moe_finalize(**kw, out=out), iters_small,
-            kernel=describe(M.OP_FINALIZE, wl.T, wl.H, wl.top_k))
+            kernel=describe(M.OP_FINALIZE, wl.T, wl.H, wl.top_k), write_bytes=wl.T * wl.H * 2)
     for T in W.CONFIGS[1]["Ts"]:
         wl = W.config_workload(1, T)
         kw, _ = upload(wl, torch)
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
         measure("decode", T, wl.H, wl.top_k, bytes_plain(T, wl.H, wl.top_k),
                 lambda: M.moe_finalize(**kw, out=out), iters_small,
-                kernel=describe(M.OP_FINALIZE, T, wl.H, wl.top_k))
+                kernel=describe(M.OP_FINALIZE, T, wl.H, wl.top_k), write_bytes=T * wl.H * 2)
     for T in (1, 16):                      # the Kimi K2.5 decode shape (H 7168, 384 experts)
         wl = W.make_workload(T, 7168, 384, 8, rsf=2.5, seed=W.default_seed(9, T))
         kw, _ = upload(wl, torch)
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
         measure("decode_H7168_E384", T, wl.H, wl.top_k, bytes_plain(T, wl.H, wl.top_k),
                 lambda: M.moe_finalize(**kw, out=out), iters_small,
-                kernel=describe(M.OP_FINALIZE, T, wl.H, wl.top_k))
+                kernel=describe(M.OP_FINALIZE, T, wl.H, wl.top_k), write_bytes=T * wl.H * 2)
     wl = W.config_workload(2)
     for packed in (False, True):
         kw, _ = upload(wl, torch, packed=packed)
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
         measure("packed" if packed else "fp32_weights", wl.T, wl.H, wl.top_k,
                 bytes_plain(wl.T, wl.H, wl.top_k), lambda: M.moe_finalize(**kw, out=out),
-                iters_small, kernel=describe(M.OP_FINALIZE, wl.T, wl.H, wl.top_k))
+                iters_small, kernel=describe(M.OP_FINALIZE, wl.T, wl.H, wl.top_k),
+                write_bytes=wl.T * wl.H * 2)
     for T in W.CONFIGS[3]["Ts"]:
         wl = W.config_workload(3, T)
         kw, ex = upload(wl, torch)
@@ -388,7 +390,8 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
         measure("residual_rmsnorm", T, wl.H, wl.top_k, bytes_rmsnorm(T, wl.H, wl.top_k),
                 lambda: M.moe_finalize_residual_rmsnorm(**kw, **ex, residual_out=ro, normed=nm),
                 iters_big if T >= 1024 else iters_small,
-                kernel=describe(M.OP_RESIDUAL_RMSNORM, T, wl.H, wl.top_k))
+                kernel=describe(M.OP_RESIDUAL_RMSNORM, T, wl.H, wl.top_k),
+                write_bytes=2 * T * wl.H * 2)
     for T in (1, 256, 8192):
         E, k = 256, 8
         lg = torch.from_numpy(W.router_logits(T, E, seed=T)).to("cuda:0")
@@ -397,7 +400,8 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
         gp = torch.empty((T, k), dtype=torch.int32, device="cuda:0")
         measure("topk_sigmoid_gate", T, E, k, T * (4 * E + 12 * k),
                 lambda: M.moe_topk_sigmoid_gate(lg, k, topk_ids=gi, topk_weights=gw,
-                                                topk_packed=gp), iters_small)
+                                                topk_packed=gp), iters_small,
+                write_bytes=T * 12 * k)
     for T in (16, 8192):
         H = 7168
         xa = torch.from_numpy(W.activations(T, H, seed=T).view(np.int16)).view(
@@ -406,9 +410,11 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
         a8 = torch.empty((T, H // 128), dtype=torch.uint8, device="cuda:0")
         af = torch.empty((T, H // 128), dtype=torch.float32, device="cuda:0")
         measure("act_quant_ue8m0", T, H, 0, T * (3 * H + H // 128),
-                lambda: M.moe_act_quant_fp8_ue8m0(xa, out_e4m3=aq, scale_e8m0=a8), iters_small)
+                lambda: M.moe_act_quant_fp8_ue8m0(xa, out_e4m3=aq, scale_e8m0=a8), iters_small,
+                write_bytes=T * (H + H // 128))
         measure("act_quant_amax", T, H, 0, T * (3 * H + 4 * (H // 128)),
-                lambda: M.moe_act_quant_fp8_amax(xa, out_e4m3=aq, scale_f32=af), iters_small)
+                lambda: M.moe_act_quant_fp8_amax(xa, out_e4m3=aq, scale_f32=af), iters_small,
+                write_bytes=T * (H + 4 * (H // 128)))
     T, H, R = 8192, 7168, 4
     parts = torch.from_numpy(W.activations(R * T, H, seed=R, log2_mag=None).view(np.int16)).view(
         torch.bfloat16).to("cuda:0").view(R, T, H)
@@ -416,7 +422,8 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
         torch.bfloat16).to("cuda:0")
     ep_out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda:0")
     measure("ep_combine_R4", T, H, 0, T * H * 2 * (R + 2),
-            lambda: M.moe_finalize_ep_combine(parts, shared_out=shp, out=ep_out), iters_big)
+            lambda: M.moe_finalize_ep_combine(parts, shared_out=shp, out=ep_out), iters_big,
+            write_bytes=T * H * 2)
     del parts, shp, ep_out
     R, H = 8, 7168
     for T in (1, 16, 256, 2048):
@@ -430,14 +437,15 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
         measure("allreduce_residual_rmsnorm_R8", T, H, 0, T * 2 * H * (R + 3) + 2 * H,
                 lambda: M.moe_allreduce_residual_rmsnorm(ranks, residual=ares, gamma=agam,
                                                          residual_out=aro, normed=anm),
-                iters_big if T >= 2048 else iters_small)
+                iters_big if T >= 2048 else iters_small, write_bytes=2 * T * H * 2)
         del ranks, ares, aro, anm
     n = 8192 * 8
     pk = torch.from_numpy(W.config_workload(0).packed.reshape(-1).repeat(n // 2)).to("cuda:0")
     ids = torch.empty_like(pk)
     wts = torch.empty(pk.shape, dtype=torch.float32, device="cuda:0")
     measure("packed_decode", 8192, 0, 8, 12 * n,
-            lambda: M.moe_topk_packed_decode(pk, expert_ids=ids, weights=wts), iters_small)
+            lambda: M.moe_topk_packed_decode(pk, expert_ids=ids, weights=wts), iters_small,
+            write_bytes=8 * n)
     del flush_src, flush_sink
     torch.cuda.empty_cache()
     return rows
@@ -552,13 +560,34 @@ def _stats(us):
             "p90": float(np.percentile(us, 90))}
 
 
+def _case_blocks(rows):
+    """A run's dispatches split at the sweep's marker launches (the empty
+    kernel on two 64-lane workgroups): one list per sweep case, in order."""
+    blocks, cur = [], None
+    for r in rows:
+        if r["name"] == "empty_probe_kernel" and r["grid"] == 128:
+            cur = []
+            blocks.append(cur)
+        elif cur is not None:
+            cur.append(r)
+    return blocks
+
+
+def _launches_per_call(kernel):
+    """Launches per call from the library's launch description
+    ("name<...> launches=2 grid=..."); one for kernels it does not plan."""
+    if kernel and " launches=" in kernel:
+        return max(1, int(kernel.split(" launches=")[1].split()[0]))
+    return 1
+
+
 def summarize_trace(trace_csv, bench_json, out_dir, command):
     """The kernel trace of one `bench.py` run: the timed launches of the
     headline call, and per sweep case the kernel's durations split into warm
     dispatches and cold ones (those right after the 1 GiB read-only flush)."""
     rows = _read_trace(trace_csv)
     line = _last_json_line(bench_json)
-    srcs = kernel_source_hash()
+    srcs = line.get("kernel_source_sha256") or kernel_source_hash()
     # headline: the first warmup + steps dispatches of the timed kernel
     kname = line["roofline"]["kernel"].split(" launches=")[0]
     grid = line["roofline"]["kernel"].split(" grid=")[1].split()[0]
@@ -587,14 +616,7 @@ def summarize_trace(trace_csv, bench_json, out_dir, command):
            f"({(line['roofline']['kernel_us_avg'] / avg - 1) * 100:+.1f}% against the trace).", ""]
     with open(os.path.join(out_dir, "prefill_quant_T8192_H7168_kernel_trace.md"), "w") as f:
         f.write("\n".join(hl))
-    # sweep: blocks between marker dispatches, in the order of the sweep rows
-    blocks, cur = [], None
-    for r in rows:
-        if r["name"] == "empty_probe_kernel" and r["grid"] == 128:
-            cur = []
-            blocks.append(cur)
-        elif cur is not None:
-            cur.append(r)
+    blocks = _case_blocks(rows)
     sw = line.get("sweep", [])
     out = ["# Kernel durations of every bench sweep case (rocprofv3 kernel trace)", "",
            "Same run and command as `prefill_quant_T8192_H7168_kernel_trace.md`:", "",
@@ -643,11 +665,15 @@ def summarize_trace(trace_csv, bench_json, out_dir, command):
     return summary
 
 
-def summarize_counters(fetch_csv, write_csv, out_dir, commands):
+def summarize_counters(fetch_csv, write_csv, out_dir, commands, bench_json=None):
     """The two counter passes of `bench.py --copy-calibration --no-sweep`:
     FETCH_SIZE and WRITE_SIZE of the three 1 GiB device copies (the factor
-    that turns each counter into bytes) and of the headline launches."""
+    that turns each counter into bytes) and of the headline launches. The
+    kernel source hash is the one a pass's JSON line records, when given."""
     import csv
+    srcs = kernel_source_hash()
+    if bench_json is not None:
+        srcs = _last_json_line(bench_json).get("kernel_source_sha256") or srcs
 
     def read(path, counter):
         d = {}
@@ -673,7 +699,7 @@ def summarize_counters(fetch_csv, write_csv, out_dir, commands):
     j = {"kernel": qname,
          "workload": "prefill finalize + UE8M0/E4M3, T=8192, H=7168, E=256, top_k=8, fp32 "
                      "weights, shared expert",
-         "kernel_source_sha256": kernel_source_hash(),
+         "kernel_source_sha256": srcs,
          "fetch_size_kib_per_launch": fk, "write_size_kib_per_launch": wk,
          "copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
                               "fetch_size_kib": float(np.median(cf)),
@@ -709,6 +735,194 @@ def summarize_counters(fetch_csv, write_csv, out_dir, commands):
     return j
 
 
+def _read_counters(path):
+    """Per dispatch of a rocprofv3 counter pass: kernel, grid and the summed
+    value of each counter collected."""
+    import csv
+    d = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            k = int(r["Dispatch_Id"])
+            e = d.setdefault(k, {"name": _short_kernel(r["Kernel_Name"]), "grid": int(r["Grid_Size"]),
+                                 "id": k, "c": {}})
+            e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [d[k] for k in sorted(d)]
+
+
+def _sweep_case_counters(rows, sweep):
+    """Per sweep case: the case's kernel (the name with the most dispatches in
+    its block, flush kernels aside) and each counter's mean per call (the sum
+    over the kernel's dispatches divided by the calls, a call being as many
+    dispatches as the library's plan launches)."""
+    out = []
+    for case, blk in zip(sweep, _case_blocks(rows)):
+        by = {}
+        for r in blk:
+            if r["name"] != "read_probe_kernel":
+                by.setdefault(r["name"], []).append(r)
+        if not by:
+            continue
+        name = max(by, key=lambda n: len(by[n]))
+        calls = len(by[name]) / _launches_per_call(case.get("kernel"))
+        tot = {}
+        for r in by[name]:
+            for c, v in r["c"].items():
+                tot[c] = tot.get(c, 0.0) + v
+        out.append({"case": case, "kernel": name, "dispatches": len(by[name]),
+                    "per_call": {c: v / calls for c, v in tot.items()}})
+    return out
+
+
+def summarize_sweep_counters(bench_json, counter_csvs, out_dir, commands, trace_csv=None):
+    """Counter passes over a whole `bench.py --copy-calibration` run (sweep
+    included). With FETCH_SIZE and WRITE_SIZE passes: HBM bytes per call of
+    every sweep case against its algorithmic bytes, each counter scaled by
+    what it reads for the run's three 1 GiB copies. With an SQ pass
+    (SQ_WAVES, SQ_INSTS_VALU, SQ_INSTS_SALU): instructions per wave and the
+    time vector issue alone needs, beside the warm median of the kernel
+    trace `trace_csv` when given."""
+    line = _last_json_line(bench_json)
+    sweep = line.get("sweep", [])
+    passes = [_read_counters(p) for p in counter_csvs]
+    names = set()
+    for rows in passes:
+        for r in rows:
+            names.update(r["c"])
+    srcs = line.get("kernel_source_sha256") or kernel_source_hash()
+    head = ["Commands (from `/tmp` with `TMPDIR=/tmp` on the MI355X box; `$R` is the repository "
+            "root there), each in its own run:", ""] + [f"    {c}" for c in commands] + [
+            "", "Written by `python bench.py --summarize-sweep-counters`. A sweep case's calls are "
+            "its warm-up, back-to-back, cold (after a 1 GiB read-only flush), batched and "
+            "graph-replayed calls; each figure is the mean per call over all of them.", "",
+            f"Kernel source SHA-256 (`finalize_kernels.hip` + `device_common.h` + "
+            f"`moef_internal.h`): `{srcs}`", ""]
+    written = {}
+    if "FETCH_SIZE" in names and "WRITE_SIZE" in names:
+        per = {}
+        factor = {}
+        for rows in passes:
+            for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+                cal = [r["c"][ctr] for r in rows
+                       if r["name"] == "__amd_rocclr_copyBuffer" and ctr in r["c"]][:3]
+                if cal:
+                    factor[ctr] = (1 << 30) / (float(np.median(cal)) * 1024)
+                    for e in _sweep_case_counters(rows, sweep):
+                        per.setdefault(e["case"]["case"] + f" T={e['case']['T']}", {}).update(
+                            {"case": e["case"], "kernel": e["kernel"],
+                             "dispatches": e["dispatches"],
+                             ctr: e["per_call"][ctr] * 1024 * factor[ctr]})
+        if set(factor) != {"FETCH_SIZE", "WRITE_SIZE"}:
+            raise ValueError("FETCH_SIZE and WRITE_SIZE passes need the --copy-calibration copies")
+        md = ["# HBM traffic of every bench sweep case (rocprofv3 FETCH_SIZE / WRITE_SIZE)", ""]
+        md += head
+        md += [f"Calibration (1 GiB / counter reading of the three copies): fetch "
+               f"{factor['FETCH_SIZE']:.6f}, write {factor['WRITE_SIZE']:.6f}.", "",
+               "| case | kernel | dispatches | algorithmic read MB | counter read MB | read ratio "
+               "| algorithmic write MB | counter write MB | write ratio |",
+               "|---|---|---|---|---|---|---|---|---|"]
+        rows_out = []
+        for key, e in per.items():
+            c = e["case"]
+            if "FETCH_SIZE" not in e or "WRITE_SIZE" not in e or not c["algorithmic_bytes"]:
+                continue
+            wb = c.get("algorithmic_write_bytes")
+            rb = c["algorithmic_bytes"] - wb if wb is not None else None
+            label = f"{c['case']} T={c['T']} H={c['H']} k={c['top_k']}"
+            fr, fw = e["FETCH_SIZE"], e["WRITE_SIZE"]
+            md.append(f"| {label} | `{e['kernel']}` | {e['dispatches']} | "
+                      f"{rb / 1e6 if rb is not None else float('nan'):,.3f} | {fr / 1e6:,.3f} | "
+                      f"{fr / rb if rb else float('nan'):.4f} | "
+                      f"{wb / 1e6 if wb is not None else float('nan'):,.3f} | {fw / 1e6:,.3f} | "
+                      f"{fw / wb if wb else float('nan'):.4f} |")
+            rows_out.append({"case": label, "kernel": e["kernel"], "read_bytes": fr,
+                             "write_bytes": fw, "algorithmic_read_bytes": rb,
+                             "algorithmic_write_bytes": wb})
+        with open(os.path.join(out_dir, "finalize_sweep_counters.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
+        written["hbm"] = rows_out
+    if {"SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU"} <= names:
+        warm = {}
+        if trace_csv:
+            for case, blk in zip(sweep, _case_blocks(_read_trace(trace_csv))):
+                by = {}
+                prev = None
+                for r in blk:
+                    if r["name"] != "read_probe_kernel" and not (
+                            prev is not None and prev["name"] == "read_probe_kernel"):
+                        by.setdefault(r["name"], []).append(r["us"])
+                    prev = r
+                if by:
+                    n = max(by, key=lambda k: sum(by[k]))
+                    warm[case["case"] + f" T={case['T']}"] = (
+                        float(np.median(by[n])) * _launches_per_call(case.get("kernel")))
+        md = ["# Instructions per wave and the vector-issue bound of every sweep case "
+              "(rocprofv3 SQ counters)", ""]
+        md += head
+        md += ["A wave64 vector instruction occupies a 16-lane SIMD for 4 cycles, and the chip "
+               "has 1024 SIMDs at 2.4 GHz, so the vector instructions of one call alone need "
+               "VALU × 4 / (1024 × 2.4e9) s (the **VALU issue bound**). The time column is the "
+               "warm median per call of the kernel trace named above (launches per call × the "
+               "median dispatch).", "",
+               "| case | kernel | waves | VALU / wave | SALU / wave | VALU issue bound µs | "
+               "trace median µs | bound / time |", "|---|---|---|---|---|---|---|---|"]
+        rows_out = []
+        kd = line.get("roofline", {}).get("kernel", "")
+        hname, hgrid = kd.split(" launches=")[0], None
+        if " grid=" in kd:
+            nwg, wg = (int(x) for x in kd.split(" grid=")[1].split()[0].split("x"))
+            hgrid = nwg * wg
+        for rows in passes:
+            if not any("SQ_WAVES" in r["c"] for r in rows):
+                continue
+            # the headline launches: before the sweep's first marker
+            head = []
+            for r in rows:
+                if r["name"] == "empty_probe_kernel" and r["grid"] == 128:
+                    break
+                if r["name"] == hname and r["grid"] == hgrid:
+                    head.append(r)
+            if head:
+                tot = {c: sum(r["c"].get(c, 0.0) for r in head) / len(head)
+                       for c in ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU")}
+                t = None
+                if trace_csv:
+                    tr = [r["us"] for r in _read_trace(trace_csv)
+                          if r["name"] == hname and r["grid"] == hgrid]
+                    t = float(np.median(tr)) if tr else None
+                cfg = line.get("config", {})
+                label = (f"headline T={cfg.get('tokens')} H={cfg.get('hidden')} "
+                         f"k={cfg.get('top_k')} (one launch)")
+                waves = tot["SQ_WAVES"]
+                bound = tot["SQ_INSTS_VALU"] * 4 / (1024 * 2.4e9) * 1e6
+                md.append(f"| {label} | `{hname}` | {waves:,.0f} | "
+                          f"{tot['SQ_INSTS_VALU'] / waves:,.0f} | {tot['SQ_INSTS_SALU'] / waves:,.0f} "
+                          f"| {bound:.2f} | {t if t else float('nan'):.3f} | "
+                          f"{bound / t * 100 if t else float('nan'):.0f}% |")
+                rows_out.append({"case": label, "kernel": hname, "waves": waves,
+                                 "valu_per_wave": tot["SQ_INSTS_VALU"] / waves,
+                                 "salu_per_wave": tot["SQ_INSTS_SALU"] / waves,
+                                 "valu_bound_us": bound, "trace_median_us": t})
+            for e in _sweep_case_counters(rows, sweep):
+                c, pc = e["case"], e["per_call"]
+                if not pc.get("SQ_WAVES"):
+                    continue
+                waves = pc["SQ_WAVES"]
+                valu, salu = pc["SQ_INSTS_VALU"] / waves, pc["SQ_INSTS_SALU"] / waves
+                bound = pc["SQ_INSTS_VALU"] * 4 / (1024 * 2.4e9) * 1e6
+                t = warm.get(c["case"] + f" T={c['T']}")
+                label = f"{c['case']} T={c['T']} H={c['H']} k={c['top_k']}"
+                md.append(f"| {label} | `{e['kernel']}` | {waves:,.0f} | {valu:,.0f} | {salu:,.0f} "
+                          f"| {bound:.2f} | {t if t else float('nan'):.3f} | "
+                          f"{bound / t * 100 if t else float('nan'):.0f}% |")
+                rows_out.append({"case": label, "kernel": e["kernel"], "waves": waves,
+                                 "valu_per_wave": valu, "salu_per_wave": salu,
+                                 "valu_bound_us": bound, "trace_median_us": t})
+        with open(os.path.join(out_dir, "finalize_sweep_instruction_counters.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
+        written["sq"] = rows_out
+    return written
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -723,9 +937,15 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"),
                     help="CPU only: write the kernel-trace summaries under profiles/ from a "
                          "rocprofv3 kernel trace of this script and its JSON line")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="CPU only: write the counter summary under profiles/ from the "
-                         "FETCH_SIZE and WRITE_SIZE passes")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="FILE",
+                    help="CPU only: FETCH_CSV WRITE_CSV [BENCH_JSON]: write the counter summary "
+                         "under profiles/ from the FETCH_SIZE and WRITE_SIZE passes (the kernel "
+                         "source hash from a pass's JSON line when given)")
+    ap.add_argument("--summarize-sweep-counters", nargs="+", metavar="FILE",
+                    help="CPU only: BENCH_JSON COUNTER_CSV... [--trace TRACE_CSV]: write the "
+                         "per-case counter summaries of a run with the sweep under profiles/")
+    ap.add_argument("--trace", help="with --summarize-sweep-counters: a kernel trace of the "
+                                    "same command, for the time column")
     ap.add_argument("--command", action="append", default=[],
                     help="the command that made the summarized data (recorded verbatim)")
     args = ap.parse_args()
@@ -734,7 +954,12 @@ def main():
         summarize_trace(*args.summarize_trace, out_dir, " ".join(args.command) or "(not given)")
         return
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, out_dir, args.command or ["(not given)"])
+        f, w, *bj = args.summarize_counters
+        summarize_counters(f, w, out_dir, args.command or ["(not given)"], bj[0] if bj else None)
+        return
+    if args.summarize_sweep_counters:
+        bj, *csvs = args.summarize_sweep_counters
+        summarize_sweep_counters(bj, csvs, out_dir, args.command or ["(not given)"], args.trace)
         return
 
     if args.gpus != 1:
@@ -813,6 +1038,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "kernel_source_sha256": kernel_source_hash(),
         "config": {"workload": "prefill_finalize_fp8_ue8m0", "tokens": T, "hidden": H,
                    "experts": wl.E, "top_k": k, "padded_rows": wl.P,
                    "routed_scaling_factor": wl.rsf, "shared_expert": True,

@@ -75,8 +75,10 @@ struct GatherArgs {
 // routing-independent operands (shared, residual) first, then the token's
 // row indices, then the row loads they address, and only then the weights,
 // which the compiler can fetch while the rows are in flight. Nothing
-// branches between the index load and the row loads (an out-of-range index
-// is reported after the store, by report_out_of_range).
+// branches between the index load and the row loads, nor between the loads
+// and the adds: a skipped slot loads zeros through an empty buffer range and
+// adds -0 (an out-of-range index is reported after the store, by
+// report_out_of_range).
 
 // The token's gathered rows, or -1 where a slot is skipped: an index < 0
 // names an expert that is not local, one >= num_rows is out of range (the
@@ -98,17 +100,32 @@ __device__ __forceinline__ bool load_rows(const GatherArgs& a, int t, int32_t ro
   return oob;
 }
 
+// Word 3 of a gfx9-family buffer resource for untyped loads (32-bit data
+// format, no swizzle, no index stride), and the non-temporal cache policy.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferNonTemporal = 2;
+
+// One 16-byte vector of gathered row `row` (wave-uniform) at column vector
+// col < h8, non-temporal. The load goes through a buffer resource that spans
+// exactly that row, or nothing when row < 0: the hardware's range check then
+// returns zeros without a memory access, so a skipped slot costs no branch.
+__device__ __forceinline__ u32x4 load_row_vector(const u32x4* g2, int32_t row, int32_t h8,
+                                                 int64_t col) {
+  const bool take = row >= 0;
+  const u32x4* base = g2 + (int64_t)(take ? row : 0) * h8;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4*>(base), 0, take ? h8 * 16 : 0, kBufferWord3);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)col * 16, 0, kBufferNonTemporal);
+}
+
 // The 16-byte vectors of the token's rows at column vector col, every load
-// issued before any is used.
+// issued before any is used; zeros for a skipped slot.
 template <int KMAX, bool EXACT>
 __device__ __forceinline__ void load_gathers(const GatherArgs& a, int64_t col,
                                              const int32_t row[KMAX], u32x4 v[KMAX]) {
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    v[j] = u32x4{0u, 0u, 0u, 0u};
-    if ((EXACT || j < a.k) && row[j] >= 0)
-      v[j] = __builtin_nontemporal_load(a.g2 + (int64_t)row[j] * a.h8 + col);
-  }
+  for (int j = 0; j < KMAX; ++j)
+    v[j] = load_row_vector(a.g2, (EXACT || j < a.k) ? row[j] : -1, a.h8, col);
 }
 
 // w' = fp32(w * rsf) per slot, from fp32 weights or the bf16 half of packed
@@ -151,7 +168,9 @@ __device__ __forceinline__ Side load_side(const GatherArgs& a, int t, int64_t co
 
 // acc[0..7] for columns [8*col, 8*col + 8): the weighted sum of the gathered
 // rows in slot order, then + shared, then + residual (when given), each step
-// in fp32.
+// in fp32. A skipped slot's vector is zeros (load_gathers) and its weight is
+// taken as -0, so its product is -0 and acc + (-0) == acc for every acc,
+// +0 and -0 included: the sum over the taken slots, with no branch.
 template <int KMAX, bool EXACT>
 __device__ __forceinline__ void reduce_rows(const GatherArgs& a, const int32_t row[KMAX],
                                             const u32x4 v[KMAX], const float w[KMAX],
@@ -160,12 +179,11 @@ __device__ __forceinline__ void reduce_rows(const GatherArgs& a, const int32_t r
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    if ((EXACT || j < a.k) && row[j] >= 0) {
-      float x[8];
-      unpack8(v[j], x);
+    const float wj = ((EXACT || j < a.k) && row[j] >= 0) ? w[j] : -0.0f;
+    float x[8];
+    unpack8(v[j], x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + w[j] * x[e];
-    }
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + wj * x[e];
   }
   if (a.shared != nullptr) {
     float x[8];

@@ -103,10 +103,13 @@ constexpr int64_t kStagedFromUnitsPerCu = 80;
 // From kStagedTailFromUnitsPerCu units per CU, the last kStagedTailPercent of
 // each group's units go to workgroups beyond the one per CU, one unit per
 // wave, which the dispatcher starts on the CUs that finish their share first
-// (finalize_quant_staged_kernel). Measured at H = 7168: T = 8192 (448 units
-// per CU) 172.4 -> 169.0 us; T = 2048 (112 per CU) 44.4 -> 44.8 us.
+// (finalize_quant_staged_kernel). Measured at H = 7168 (kernel-trace medians
+// without -> with): T = 2048 (112 units per CU) 44.4 -> 44.8 us; T = 2560
+// (140) 55.9 -> 55.8; T = 3072 (168) 65.9 -> 64.9; T = 3584 (196) 76.7 ->
+// 74.9; T = 4096 (224) 88.3 -> 86.6; T = 6144 131.0 -> 128.0; T = 8192 (448)
+// 172.9 -> 169.1.
 constexpr int kStagedTailPercent = 5;
-constexpr int64_t kStagedTailFromUnitsPerCu = 256;
+constexpr int64_t kStagedTailFromUnitsPerCu = 160;
 constexpr int kStagedMaxTopK = 8;
 static_assert(kStageUnits * kStageUnitBytes + 4 <= kLdsPerCu, "staging fits the CU's LDS");
 // The plain finalize stages the same way: 1 KiB of bf16 output per unit, 159

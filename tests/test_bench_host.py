@@ -134,3 +134,67 @@ def test_cpu_leg_on_a_thread_pool():
     assert base["single_thread"]["value"] > 0
     assert "3 threads" in base["sample"]
     assert 1 <= bench.host_threads() <= 16
+
+
+def _counter_csv(path, dispatches, counter):
+    """A rocprofv3 counter-collection CSV: (kernel name, grid, value) per
+    dispatch, each value split over two rows as the per-instance rows are."""
+    cols = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+            "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+            "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+            "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    lines = [",".join(f'"{c}"' for c in cols)]
+    for i, (name, grid, vals) in enumerate(dispatches, 1):
+        for ctr, v in vals.items():
+            if counter is not None and ctr != counter:
+                continue
+            for half in (0.25 * v, 0.75 * v):
+                lines.append(f'{i},{i},"Agent 1",1,1,1,{grid},1,"{name}",256,0,0,8,0,16,'
+                             f'"{ctr}",{half},{1000 * i},{1000 * i + 500}')
+    path.write_text("\n".join(lines) + "\n")
+
+
+def test_sweep_counter_summary(tmp_path, monkeypatch):
+    """Cases split at the marker launches; the copies calibrate each counter
+    (here FETCH_SIZE reads half the bytes, as it does for 128-byte requests);
+    a call of a two-launch kernel counts both dispatches; flush kernels and
+    the markers are left out."""
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h" * 64)
+    copy = ("__amd_rocclr_copyBuffer", 1 << 20, {"FETCH_SIZE": 524288.0, "WRITE_SIZE": 1048576.0})
+    mark = ("void (anonymous namespace)::empty_probe_kernel()", 128, {"FETCH_SIZE": 0.0,
+                                                                        "WRITE_SIZE": 0.0})
+    flush = ("void (anonymous namespace)::read_probe_kernel(uint4 const*, unsigned int*)", 1 << 26,
+             {"FETCH_SIZE": 1e6, "WRITE_SIZE": 0.0})
+    one = ("void moef::finalize_kernel<8, true>(moef::GatherArgs, uint4*)", 4096,
+           {"FETCH_SIZE": 50.0, "WRITE_SIZE": 10.0})
+    two = ("void moef::finalize_rmsnorm_staged_kernel<8, true>(moef::GatherArgs)", 65536,
+           {"FETCH_SIZE": 500.0, "WRITE_SIZE": 300.0})
+    d = [copy, copy, copy, mark, one, one, flush, one, mark, two, two, flush, two, two]
+    _counter_csv(tmp_path / "f.csv", d, "FETCH_SIZE")
+    _counter_csv(tmp_path / "w.csv", d, "WRITE_SIZE")
+    sweep = [{"case": "decode", "T": 1, "H": 4096, "top_k": 8, "algorithmic_bytes": 110 * 1024,
+              "algorithmic_write_bytes": 10 * 1024, "kernel": "finalize_kernel<8, true> launches=1 grid=1"},
+             {"case": "residual_rmsnorm", "T": 4096, "H": 7168, "top_k": 8,
+              "algorithmic_bytes": 2600 * 1024, "algorithmic_write_bytes": 600 * 1024,
+              "kernel": "finalize_rmsnorm_staged_kernel<8, true> launches=2 grid=256x1024"}]
+    (tmp_path / "b.json").write_text("log line\n" + json.dumps({"sweep": sweep}) + "\n")
+    out = bench.summarize_sweep_counters(str(tmp_path / "b.json"),
+                                         [str(tmp_path / "f.csv"), str(tmp_path / "w.csv")],
+                                         str(tmp_path), ["cmd one", "cmd two"])
+    hbm = {r["case"].split()[0]: r for r in out["hbm"]}
+    assert hbm["decode"]["kernel"] == "finalize_kernel<8, true>"
+    assert hbm["decode"]["read_bytes"] == pytest.approx(100 * 1024)
+    assert hbm["decode"]["write_bytes"] == pytest.approx(10 * 1024)
+    assert hbm["residual_rmsnorm"]["read_bytes"] == pytest.approx(2000 * 1024)
+    assert hbm["residual_rmsnorm"]["write_bytes"] == pytest.approx(600 * 1024)
+    text = (tmp_path / "finalize_sweep_counters.md").read_text()
+    assert "cmd one" in text and "cmd two" in text and "1.0000" in text
+    sq = ("void moef::finalize_kernel<8, true>(moef::GatherArgs, uint4*)", 4096,
+          {"SQ_WAVES": 64.0, "SQ_INSTS_VALU": 64.0 * 300, "SQ_INSTS_SALU": 64.0 * 100})
+    sq_mark = (mark[0], 128, {"SQ_WAVES": 1.0, "SQ_INSTS_VALU": 0.0, "SQ_INSTS_SALU": 2.0})
+    _counter_csv(tmp_path / "sq.csv", [sq_mark, sq, sq, sq_mark], None)
+    out = bench.summarize_sweep_counters(str(tmp_path / "b.json"), [str(tmp_path / "sq.csv")],
+                                         str(tmp_path), ["cmd"])
+    r = out["sq"][0]
+    assert r["waves"] == 64 and r["valu_per_wave"] == 300 and r["salu_per_wave"] == 100
+    assert r["valu_bound_us"] == pytest.approx(64 * 300 * 4 / (1024 * 2.4e9) * 1e6)

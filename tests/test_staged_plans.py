@@ -287,6 +287,11 @@ def describe(L, op, T, H, k, ncu):
      "finalize_quant_staged_kernel<8, true, 12> launches=1 grid=616x1024 groups=8 tail=5%"),
     (2, 2048, 7168, 8, 256,
      "finalize_quant_staged_kernel<8, true, 0> launches=1 grid=256x1024 groups=8 tail=0%"),
+    # tail workgroups from 160 units per CU: T = 3072 is 168 per CU, T = 2560 is 140
+    (2, 3072, 7168, 8, 256,
+     "finalize_quant_staged_kernel<8, true, 0> launches=1 grid=392x1024 groups=8 tail=5%"),
+    (2, 2560, 7168, 8, 256,
+     "finalize_quant_staged_kernel<8, true, 0> launches=1 grid=256x1024 groups=8 tail=0%"),
     (2, 1024, 7168, 8, 256, "finalize_quant_kernel<8, true> launches=1 grid=3584x256"),
     (2, 8192, 7168, 16, 256, "finalize_quant_kernel<16, false> launches=1 grid=28672x256"),
     (0, 1, 4096, 8, 256, "finalize_kernel<8, true> launches=1 grid=2x256"),
