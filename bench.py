@@ -625,14 +625,16 @@ def summarize_trace(trace_csv, bench_json, out_dir, command):
            "launch; its dispatches are 5 warm-up calls, back-to-back calls, calls each after a "
            "1 GiB read-only stream through the caches (**cold**: the dispatch right after the "
            "flush kernel), 100 back-to-back calls and 20-call HIP-graph replays. **Warm** is "
-           "every dispatch of the case's kernel that does not follow a flush. The first row, the "
-           "empty kernel (one wave, no memory access), is the floor under every other row, in "
-           "the same two states.", "",
+           "every dispatch of the case's kernel that does not follow a flush; **graph** is the "
+           "last 10 replays of the 20-call graph (200 calls back to back, the way a captured "
+           "model runs them), per call (launches per call × the median dispatch). The first "
+           "row, the empty kernel (one wave, no memory access), is the floor under every other "
+           "row, in the same states.", "",
            f"Kernel source SHA-256 (`finalize_kernels.hip` + `device_common.h` + "
            f"`moef_internal.h`): `{srcs}`", "",
            "| case | kernel | grid | warm n | warm median µs | p10 | p90 | cold n | cold median µs "
-           "| algorithmic bytes | GB/s warm | GB/s cold |",
-           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+           "| graph µs/call | algorithmic bytes | GB/s warm | GB/s cold | GB/s graph |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     summary = []
     for case, blk in zip(sw, blocks):
         by = {}
@@ -651,15 +653,20 @@ def summarize_trace(trace_csv, bench_json, out_dir, command):
                 (cold if prev is not None and prev["name"] == "read_probe_kernel" else warm).append(r["us"])
             prev = r
         w, c = _stats(warm), _stats(cold)
+        lpc = _launches_per_call(case.get("kernel"))
+        tail = [r["us"] for r in blk if r["id"] in ids][-200 * lpc:]
+        g = float(np.median(tail)) * lpc if len(tail) == 200 * lpc else None
         nb = case["algorithmic_bytes"]
         label = f"{case['case']} T={case['T']} H={case['H']} k={case['top_k']}"
         gw = f"{nb / w['median'] / 1e3:,.1f}" if nb and w else "—"
         gc = f"{nb / c['median'] / 1e3:,.1f}" if nb and c else "—"
+        gg = f"{nb / g / 1e3:,.1f}" if nb and g else "—"
         out.append(f"| {label} | `{key[0]}` | {key[1]} | {w['n']} | {w['median']:.3f} | "
                    f"{w['p10']:.3f} | {w['p90']:.3f} | {c['n'] if c else 0} | "
-                   f"{c['median'] if c else float('nan'):.3f} | {nb:,} | {gw} | {gc} |")
+                   f"{c['median'] if c else float('nan'):.3f} | "
+                   f"{g if g else float('nan'):.3f} | {nb:,} | {gw} | {gc} | {gg} |")
         summary.append({"case": label, "kernel": key[0], "grid": key[1], "warm": w, "cold": c,
-                        "algorithmic_bytes": nb})
+                        "graph_us_per_call": g, "algorithmic_bytes": nb})
     with open(os.path.join(out_dir, "finalize_sweep_kernel_trace.md"), "w") as f:
         f.write("\n".join(out) + "\n")
     return summary
