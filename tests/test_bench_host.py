@@ -198,3 +198,38 @@ def test_sweep_counter_summary(tmp_path, monkeypatch):
     r = out["sq"][0]
     assert r["waves"] == 64 and r["valu_per_wave"] == 300 and r["salu_per_wave"] == 100
     assert r["valu_bound_us"] == pytest.approx(64 * 300 * 4 / (1024 * 2.4e9) * 1e6)
+
+
+def test_trace_summary(tmp_path, monkeypatch):
+    """The headline's timed launches follow its warm-up ones; a sweep case is
+    split at its marker into warm dispatches, cold ones (right after the
+    flush kernel) and the last 200 (the graph replays)."""
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h" * 64)
+    head = "void moef::finalize_quant_staged_kernel<8, true, 12>(moef::GatherArgs, uint2*)"
+    dec = "void moef::finalize_kernel<8, true>(moef::GatherArgs, uint4*)"
+    mark = "void (anonymous namespace)::empty_probe_kernel()"
+    flush = "void (anonymous namespace)::read_probe_kernel(uint4 const*, unsigned int*)"
+    d = [(head, 616 * 1024, 180.0)] + [(head, 616 * 1024, us) for us in (170.0, 172.0)]
+    d += [(mark, 128, 1.0)] + [(dec, 512, 3.0)] * 30
+    d += [(flush, 1 << 26, 150.0), (dec, 512, 5.0)] * 3 + [(dec, 512, 2.0)] * 200
+    lines = ["Kernel_Name,Grid_Size_X,Workgroup_Size_X,Dispatch_Id,Start_Timestamp,End_Timestamp"]
+    t = 0
+    for i, (n, g, us) in enumerate(d, 1):
+        lines.append(f'"{n}",{g},256,{i},{t},{t + int(us * 1000)}')
+        t += int(us * 1000) + 500
+    (tmp_path / "t.csv").write_text("\n".join(lines) + "\n")
+    line = {"warmup": 1, "steps": 2, "config": {"tokens": 8192, "hidden": 7168, "top_k": 8},
+            "roofline": {"kernel": "finalize_quant_staged_kernel<8, true, 12> launches=1 "
+                                   "grid=616x1024 groups=8 tail=5%",
+                         "algorithmic_bytes_per_launch": 1_116_667_904, "kernel_us_avg": 171.5},
+            "sweep": [{"case": "decode", "T": 1, "H": 4096, "top_k": 8,
+                       "algorithmic_bytes": 81_984,
+                       "kernel": "finalize_kernel<8, true> launches=1 grid=2x256"}]}
+    (tmp_path / "b.json").write_text(json.dumps(line) + "\n")
+    out = bench.summarize_trace(str(tmp_path / "t.csv"), str(tmp_path / "b.json"), str(tmp_path),
+                                "cmd")
+    assert len(out) == 1 and out[0]["kernel"] == "finalize_kernel<8, true>"
+    assert out[0]["cold"]["n"] == 3 and out[0]["cold"]["median"] == pytest.approx(5.0)
+    assert out[0]["warm"]["n"] == 230 and out[0]["graph_us_per_call"] == pytest.approx(2.0)
+    text = (tmp_path / "prefill_quant_T8192_H7168_kernel_trace.md").read_text()
+    assert "| 2 timed (after 1 warm-up) | 171.000 |" in text and "cmd" in text
