@@ -25,11 +25,13 @@
 //
 // Epilogues:
 //  * RMSNorm: one workgroup per token (up to 16 waves), the row stays in
-//    registers; the sum of squares of each 512-column chunk by cross-lane
-//    shuffles, then the chunk sums through LDS in chunk order, so every lane
-//    sees the same value and the result does not depend on the workgroup
-//    width. From 1024 tokens on, a token takes half as many waves with two
-//    column vectors per lane (measured faster there, slower below).
+//    registers; the sum of squares of each 512-column chunk by DPP row
+//    reductions, then the chunk sums through LDS in chunk order, so every
+//    lane sees the same value and the result does not depend on the
+//    workgroup width. From 288 tokens on, a token takes half as many waves
+//    with two column vectors per lane (measured faster there, slower at
+//    decode sizes); larger grids stage whole tokens per CU
+//    (finalize_rmsnorm_staged_kernel).
 //  * UE8M0 quant: a 1 x 128 block is 16 lanes x 8 columns, one DPP row; its
 //    absolute maximum is taken on bf16 bit patterns (packed 16-bit integer
 //    max, then four DPP row rotations), the power-of-two exponent comes from

@@ -64,7 +64,12 @@ constexpr int kChunkCols = kWaveLanes * kVecElems;     // columns per wave pass
 constexpr int kWavesPerBlock = 4;                      // plain / quant kernels
 constexpr int kNormMaxThreads = 1024;                  // RMSNorm: one block per token
 constexpr int kNormMaxChunks = MOEF_MAX_HIDDEN_RMSNORM / (kVecElems * kWaveLanes);
-constexpr int64_t kNormHalfWidthFrom = 1024;           // tokens: half-width RMSNorm blocks
+// RMSNorm, one workgroup per token: from this many tokens on, half as many
+// waves with two vectors per lane (H = 7168, kernel-trace medians, one wave
+// per chunk -> half width: T = 256 8.44 -> 8.36 us; 320 11.68 -> 11.20; 512
+// 17.04 -> 15.68; 704 23.64 -> 21.36; at T <= 64 half width is slower: T = 16
+// 4.36 -> 4.76).
+constexpr int64_t kNormHalfWidthFrom = 288;
 constexpr int64_t kActQuantPairFrom = int64_t(1) << 21;  // act quant: 2 vectors per lane
 // Occupancy cap for large launches: a launch may reserve LDS it does not use
 // so that at most `blocks` workgroups are resident on a CU at once (gfx950:

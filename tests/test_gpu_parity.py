@@ -562,9 +562,10 @@ def test_non_finite_values():
 
 def test_results_do_not_depend_on_batch_size():
     """The same tokens give the same bits whether they come in a batch of
-    1100 tokens or of 40: the RMSNorm epilogue switches to half-width
-    workgroups from 1024 tokens on, and sums its per-chunk partials in the
-    same order either way. Plain and quant outputs are checked too."""
+    1100 tokens or of 40: at 1100 tokens the RMSNorm epilogue stages whole
+    tokens per CU, at 40 it runs one workgroup per token, and both sum the
+    per-chunk partials in the same order. Plain and quant outputs are checked
+    too (staged at 1100 tokens, one wave per unit at 40)."""
     T, n = 1100, 40
     wl = W.make_workload(T, 7168, 256, 8, rsf=2.5, seed=77, with_residual=True)
     kw = device_inputs(wl)
@@ -592,14 +593,15 @@ def test_results_do_not_depend_on_batch_size():
 
 @pytest.mark.parametrize("H", [1000, 4104, 5000, 16384])
 def test_rmsnorm_half_width_ragged(H):
-    """From 1024 tokens on, a row with an even number of 512-column chunks
-    takes half-width workgroups with two vectors per lane. Ragged hidden sizes
-    there: H=1000 (2 chunks, the second vector of most lanes past the row
-    end), 4104 (9 chunks: odd, stays full width), 5000 (10 chunks, partly
-    filled), 16384 (32 chunks, the widest workgroup either way). residual_out
-    is bit-exact to the mirror, normed within one ulp of the fp64 RMSNorm, and
-    the first tokens match a 16-token call bit for bit."""
-    T, k = 1024, 4
+    """From 288 tokens on (below the staged path's 40 units per CU), a row
+    with an even number of 512-column chunks takes half-width workgroups with
+    two vectors per lane. Ragged hidden sizes there: H=1000 (2 chunks, the
+    second vector of most lanes past the row end), 4104 (9 chunks: odd, stays
+    full width), 5000 (10 chunks, partly filled), 16384 (32 chunks, the
+    widest workgroup either way). residual_out is bit-exact to the mirror,
+    normed within one ulp of the fp64 RMSNorm, and the first tokens match a
+    16-token (full-width) call bit for bit."""
+    T, k = 300, 4
     wl = W.make_workload(T, H, 32, k, rsf=2.5, seed=H, with_residual=True, log2_mag=(-4.0, 4.0))
     kw = device_inputs(wl)
     res, gam = d_bf16(wl.residual), d_bf16(wl.gamma)

@@ -301,7 +301,9 @@ def describe(L, op, T, H, k, ncu):
     (1, 16, 7168, 8, 256, "finalize_rmsnorm_kernel<8, true, 1> launches=1 grid=16x896"),
     (1, 1024, 7168, 8, 256, "finalize_rmsnorm_staged_kernel<8, true> launches=1 grid=256x1024"),
     (1, 4096, 7168, 8, 256, "finalize_rmsnorm_staged_kernel<8, true> launches=2 grid=256x1024"),
-    (1, 700, 7168, 8, 256, "finalize_rmsnorm_kernel<8, true, 1> launches=1 grid=700x896"),
+    (1, 700, 7168, 8, 256, "finalize_rmsnorm_kernel<8, true, 2> launches=1 grid=700x448"),
+    (1, 287, 7168, 8, 256, "finalize_rmsnorm_kernel<8, true, 1> launches=1 grid=287x896"),
+    (1, 288, 4104, 8, 256, "finalize_rmsnorm_kernel<8, true, 1> launches=1 grid=288x576"),
     (0, 0, 7168, 8, 256, "none (num_tokens == 0)"),
 ])
 def test_describe_launch(lib, op, T, H, k, ncu, want):
