@@ -892,11 +892,16 @@ hipError_t launch_plain_staged(const GatherArgs& a, u32x4* o, int ncu, const Pla
 }  // namespace
 
 // The count of each device is queried once and kept: it sizes the staged
-// kernels' grids.
+// kernels' grids. A failed query leaves no error behind for the launch
+// checks that follow (they read hipGetLastError).
 int device_cus(hipStream_t stream) {
   int dev = -1;
   if (stream == nullptr || hipStreamGetDevice(stream, &dev) != hipSuccess) {
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (stream != nullptr) (void)hipGetLastError();
+    if (hipGetDevice(&dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
   }
   if (dev < 0) return 0;
   if (dev < kMaxDevices) {
@@ -904,8 +909,10 @@ int device_cus(hipStream_t stream) {
     if (known > 0) return known;
   }
   int ncu = 0;
-  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
     return 0;
+  }
   if (dev < kMaxDevices && ncu > 0) g_device_cus[dev].store(ncu, std::memory_order_relaxed);
   return ncu;
 }
