@@ -620,3 +620,56 @@ def test_rmsnorm_half_width_ragged(H):
     assert np.all(np.abs(g - o) <= ulp_bf16(o)), f"H={H} normed"
     assert torch.equal(ro[:n].view(torch.int16), ro_s.view(torch.int16))
     assert torch.equal(nm[:n].view(torch.int16), nm_s.view(torch.int16))
+
+
+@pytest.mark.parametrize("T_per_cu,H,k,packed", [
+    (None, 1024, 3, False),      # one wave per unit, top_k below its template's width
+    (None, 1024, 8, True),
+    (100, 1024, 4, False),       # the staged plain, RMSNorm and quant kernels
+])
+def test_skipped_slots_ignore_their_weights(T_per_cu, H, k, packed):
+    """A slot whose index is negative or out of range is skipped whatever its
+    weight holds. NaN, +-inf and huge fp32 weights, or packed words whose bf16
+    half is NaN or inf, on skipped slots leave every output equal to the
+    oracle's, which never reads them: the gather takes such a slot's weight
+    as -0 instead of multiplying by it. Plain, residual + RMSNorm and quant
+    entry points, one-wave-per-unit and staged sizes."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    T = 40 if T_per_cu is None else T_per_cu * ncu
+    wl = W.make_workload(T, H, 16, k, rsf=2.5, seed=900 + k, pad=32, with_residual=True,
+                         log2_mag=(-4.0, 4.0))
+    rng = np.random.default_rng(900 + k)
+    idx = wl.idx.copy()
+    skip = rng.random(idx.shape) < 0.3
+    oob = (rng.random(idx.shape) < 0.05) & ~skip
+    idx[skip] = -1
+    idx[oob] = wl.P + 7
+    dead = skip | oob
+    w = wl.weights.copy()
+    w[dead] = np.array([np.nan, np.inf, -np.inf, 3.0e38], np.float32)[rng.integers(0, 4, dead.sum())]
+    pk = wl.packed.view(np.uint32).copy()
+    halves = np.array([0x7FC0, 0x7F80, 0xFF80, 0xFFC1], np.uint32)[rng.integers(0, 4, dead.sum())]
+    pk[dead] = (pk[dead] & np.uint32(0xFFFF0000)) | halves
+    wl.idx, wl.weights, wl.packed = idx, w, pk.view(np.int32)
+    wkw = dict(packed=wl.packed) if packed else dict(weights_f32=w)
+    announce(f"skipped slots with non-finite weights T={T} H={H} k={k} packed={packed}")
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = run_finalize(wl, packed=packed, err=err)
+    assert int(err.item()) == M.DEVERR_INDEX_OUT_OF_RANGE
+    mirror, _ = O.finalize_mirror(wl.gemm2_out, idx, shared=wl.shared, rsf=wl.rsf, **wkw)
+    assert_bits_equal(got, mirror, "finalize")
+    assert np.isfinite(F.bf16_to_f64(got)).all()
+    kw = device_inputs(wl, packed=packed)
+    ro, nm = M.moe_finalize_residual_rmsnorm(**kw, residual=d_bf16(wl.residual),
+                                             gamma=d_bf16(wl.gamma), eps=wl.eps)
+    q, s = M.moe_finalize_quant_ue8m0(**kw)
+    torch.cuda.synchronize()
+    m_ro, m_nm, _ = O.finalize_residual_rmsnorm_mirror(
+        wl.gemm2_out, idx, shared=wl.shared, rsf=wl.rsf, residual=wl.residual, gamma=wl.gamma,
+        eps=wl.eps, **wkw)
+    assert_bits_equal(h_bits(ro), m_ro, "residual_out")
+    g, o = F.bf16_to_f64(h_bits(nm)), F.bf16_to_f64(m_nm)
+    assert np.all(np.abs(g - o) <= ulp_bf16(o)), "normed"
+    mq, ms, _ = O.finalize_quant_mirror(wl.gemm2_out, idx, shared=wl.shared, rsf=wl.rsf, **wkw)
+    assert_bits_equal(h_u8(s), ms, "scale bytes")
+    assert_bits_equal(h_u8(q), mq, "codes")
