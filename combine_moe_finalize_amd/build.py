@@ -4,7 +4,8 @@
 
 Flags: fp-contract off (the finalize's fp32 operation order is part of its
 contract: a separate multiply and add per gathered row, no fused
-multiply-add), packed-fp32 instructions disabled, -O3, gfx950 only.
+multiply-add), packed-fp32 instructions disabled, kernel-argument preload,
+-O3, gfx950 only.
 """
 from __future__ import annotations
 
@@ -22,6 +23,12 @@ except ImportError:            # run as a script
 SOURCES = ["moef_api.hip", "finalize_kernels.hip", "routing_kernels.hip", "act_quant_kernels.hip",
            "allreduce_kernels.hip"]
 ARCH = "gfx950"
+# Kernel arguments preloaded into SGPRs at wave start (gfx950 holds up to 14
+# dwords there beside the kernel-argument pointer). A kernel with pointer and
+# scalar parameters then starts without a dependent load of its arguments;
+# the compiler adds a 256-byte prologue that loads them itself when the
+# firmware does not preload. Parameters passed as a struct are not preloaded.
+KERNARG_PRELOAD = 16
 
 
 def hipcc() -> str:
@@ -35,6 +42,7 @@ def compile_command(out: str) -> list:
     return [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}",
             "-fPIC", "-shared", "-ffp-contract=off",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", f"-amdgpu-kernarg-preload-count={KERNARG_PRELOAD}",
             "-Wall", "-Wno-unused-function",
             "-I", INCLUDE, "-I", CSRC,
             *[os.path.join(CSRC, s) for s in SOURCES],

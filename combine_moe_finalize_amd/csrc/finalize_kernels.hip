@@ -68,6 +68,41 @@ struct GatherArgs {
   int32_t* err;
 };
 
+// The one-wave-per-unit kernels take the routed call as separate parameters,
+// ordered for kernel-argument preload: the first 14 dwords (the index and
+// row pointers, the sizes that address them, rsf, then the shared and weight
+// pointers) arrive in SGPRs at wave start, so the index load that opens the
+// decode call's dependent chain waits for no kernel-argument load; the
+// output, error-flag and format arguments, needed later, are loaded from
+// memory meanwhile.
+#define MOEF_ROUTED_PARAMS                                                            \
+  const int32_t *r_idx, const u32x4 *r_g2, int32_t r_h8, int32_t r_k, int32_t r_rows,  \
+      int32_t r_nchunks, int32_t r_tokens, float r_rsf, const u32x4 *r_shared,         \
+      const uint32_t *r_w, int32_t r_packed, int32_t *r_err
+#define MOEF_ROUTED_ARGS(a)                                                           \
+  (a).idx, (a).g2, (a).h8, (a).k, (a).num_rows, (a).nchunks, (a).tokens, (a).rsf,     \
+      (a).shared, (a).w, (a).packed, (a).err
+#define MOEF_ROUTED_GATHER_ARGS                                                       \
+  routed_args(r_idx, r_g2, r_h8, r_k, r_rows, r_nchunks, r_tokens, r_rsf, r_shared, r_w, \
+              r_packed, r_err)
+
+__device__ __forceinline__ GatherArgs routed_args(MOEF_ROUTED_PARAMS) {
+  GatherArgs a;
+  a.g2 = r_g2;
+  a.num_rows = r_rows;
+  a.idx = r_idx;
+  a.w = r_w;
+  a.shared = r_shared;
+  a.rsf = r_rsf;
+  a.packed = r_packed;
+  a.tokens = r_tokens;
+  a.h8 = r_h8;
+  a.k = r_k;
+  a.nchunks = r_nchunks;
+  a.err = r_err;
+  return a;
+}
+
 // (bf16 / E4M3 conversion and packing helpers: device_common.h)
 
 // ------------------------------------------------------------- gather core
@@ -236,7 +271,8 @@ __device__ __forceinline__ bool finalize_vector(const GatherArgs& a, int t, int6
 
 template <int KMAX, bool EXACT>
 __global__ void __launch_bounds__(kWavesPerBlock * kWaveLanes)
-finalize_kernel(GatherArgs a, u32x4* __restrict__ out) {
+finalize_kernel(MOEF_ROUTED_PARAMS, u32x4* __restrict__ out) {
+  const GatherArgs a = MOEF_ROUTED_GATHER_ARGS;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   // Waves past the last unit (the grid's last workgroup) redo the last unit
@@ -267,9 +303,10 @@ finalize_kernel(GatherArgs a, u32x4* __restrict__ out) {
 
 template <int KMAX, bool EXACT, int CPT>
 __global__ void __launch_bounds__(kNormMaxThreads)
-finalize_rmsnorm_kernel(GatherArgs a, const u32x4* residual, const u32x4* __restrict__ gamma,
-                        float eps, float inv_hidden, u32x4* residual_out,
-                        u32x4* __restrict__ normed) {
+finalize_rmsnorm_kernel(MOEF_ROUTED_PARAMS, const u32x4* residual,
+                        const u32x4* __restrict__ gamma, float eps, float inv_hidden,
+                        u32x4* residual_out, u32x4* __restrict__ normed) {
+  const GatherArgs a = MOEF_ROUTED_GATHER_ARGS;
   __shared__ float partial[kNormMaxChunks];
   const int t = blockIdx.x;
   const int nthreads = blockDim.x;
@@ -415,7 +452,9 @@ finalize_rmsnorm_staged_kernel(GatherArgs a, const u32x4* residual,
 
 template <int KMAX, bool EXACT>
 __global__ void __launch_bounds__(kWavesPerBlock * kWaveLanes)
-finalize_quant_kernel(GatherArgs a, u32x2* __restrict__ out_q, uint8_t* __restrict__ scale) {
+finalize_quant_kernel(MOEF_ROUTED_PARAMS, u32x2* __restrict__ out_q,
+                      uint8_t* __restrict__ scale) {
+  const GatherArgs a = MOEF_ROUTED_GATHER_ARGS;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   // as finalize_kernel: waves past the last unit redo it and store nothing
@@ -937,7 +976,7 @@ hipError_t launch_finalize(const Routed& r, uint16_t* out, hipStream_t stream) {
     constexpr int KM = decltype(km)::value;
     constexpr bool EX = decltype(ex)::value;
     hipLaunchKernelGGL((finalize_kernel<KM, EX>), dim3(plain_blocks(a)),
-                       dim3(kWavesPerBlock * kWaveLanes), lds, stream, a, o);
+                       dim3(kWavesPerBlock * kWaveLanes), lds, stream, MOEF_ROUTED_ARGS(a), o);
     return hipGetLastError();
   });
 }
@@ -983,10 +1022,10 @@ hipError_t launch_finalize_rmsnorm(const Routed& r, const uint16_t* residual,
     constexpr bool EX = decltype(ex)::value;
     if (c.cpt == 1)
       hipLaunchKernelGGL((finalize_rmsnorm_kernel<KM, EX, 1>), dim3(a.tokens), dim3(c.threads),
-                         0, stream, a, res, gam, eps, inv_hidden, ro, nm);
+                         0, stream, MOEF_ROUTED_ARGS(a), res, gam, eps, inv_hidden, ro, nm);
     else
       hipLaunchKernelGGL((finalize_rmsnorm_kernel<KM, EX, 2>), dim3(a.tokens), dim3(c.threads),
-                         lds2, stream, a, res, gam, eps, inv_hidden, ro, nm);
+                         lds2, stream, MOEF_ROUTED_ARGS(a), res, gam, eps, inv_hidden, ro, nm);
     return hipGetLastError();
   });
 }
@@ -1017,7 +1056,8 @@ hipError_t launch_finalize_quant(const Routed& r, uint8_t* out_e4m3, uint8_t* sc
     constexpr int KM = decltype(km)::value;
     constexpr bool EX = decltype(ex)::value;
     hipLaunchKernelGGL((finalize_quant_kernel<KM, EX>), dim3(plain_blocks(a)),
-                       dim3(kWavesPerBlock * kWaveLanes), lds, stream, a, q, scale_e8m0);
+                       dim3(kWavesPerBlock * kWaveLanes), lds, stream, MOEF_ROUTED_ARGS(a), q,
+                       scale_e8m0);
     return hipGetLastError();
   });
 }

@@ -652,6 +652,7 @@ def test_skipped_slots_ignore_their_weights(T_per_cu, H, k, packed):
     pk[dead] = (pk[dead] & np.uint32(0xFFFF0000)) | halves
     wl.idx, wl.weights, wl.packed = idx, w, pk.view(np.int32)
     wkw = dict(packed=wl.packed) if packed else dict(weights_f32=w)
+    np.seterr(over="ignore")       # the oracle scales the dead slots' huge weights too
     announce(f"skipped slots with non-finite weights T={T} H={H} k={k} packed={packed}")
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     got = run_finalize(wl, packed=packed, err=err)
