@@ -281,7 +281,7 @@ def describe(L, op, T, H, k, ncu):
     return st, buf.value.decode()
 
 
-@pytest.mark.parametrize("op,T,H,k,ncu,want", [
+DESCRIBE_CASES = [
     # the prefill quant call: one staged launch, 8 XCD groups, 360 tail workgroups
     (2, 8192, 7168, 8, 256,
      "finalize_quant_staged_kernel<8, true, 12> launches=1 grid=616x1024 groups=8 tail=5%"),
@@ -305,7 +305,10 @@ def describe(L, op, T, H, k, ncu):
     (1, 287, 7168, 8, 256, "finalize_rmsnorm_kernel<8, true, 1> launches=1 grid=287x896"),
     (1, 288, 4104, 8, 256, "finalize_rmsnorm_kernel<8, true, 1> launches=1 grid=288x576"),
     (0, 0, 7168, 8, 256, "none (num_tokens == 0)"),
-])
+]
+
+
+@pytest.mark.parametrize("op,T,H,k,ncu,want", DESCRIBE_CASES)
 def test_describe_launch(lib, op, T, H, k, ncu, want):
     """The library's own description of a call's launch, planned for 256
     CUs, for the shapes the benchmark times."""
