@@ -13,33 +13,44 @@ UE8M0 / E4M3 quantization.
 Printed: one JSON line with
   value      algorithmic GB/s of the whole step (bytes the method must move /
              wall time per step, inputs resident),
+  kernel_source_sha256  the finalize kernel sources the run used,
   ceilings   same-session streaming read and copy rates (the bandwidth probe
              kernels) and torch's device copy, with the headline kernel's rate
              as a fraction of the read and copy rates (the kernel moves 95%
              reads, a copy half),
   roofline   the kernel's algorithmic bytes per launch / its average duration
              (HIP events recorded on the launch stream around the K timed
-             launches, divided by K), against the 8 TB/s HBM peak;
-             `traffic` is the counter-measured HBM bytes per launch from the
-             committed rocprofv3 counter summary when it matches the current
-             kernel source, else null,
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload,
-  sweep      microseconds per call and GB/s for the other workload shapes
-             (decode T=1..256, packed vs fp32 routing, residual + RMSNorm,
-             packed decode, the routing gate, standalone FP8 activation
-             quant in both scale policies, the expert-parallel combine of
-             four partials; for the gate the "H" field holds the expert
-             count E): per-call HIP-event times (which include a few
-             microseconds of event overhead), warm and cold (after streaming
-             a 1 GiB buffer through the caches); the sustained per-call time
-             of 100 back-to-back calls; and the per-call time of 20 calls
-             captured in a HIP graph and replayed. Kernel-only durations come
-             from rocprofv3 (see profiles/),
+             launches, divided by K), against the 8 TB/s HBM peak; `kernel`
+             is the launch as the library plans it on this device
+             (moe_finalize_describe_launch); `traffic` is the
+             counter-measured HBM bytes per launch from the committed
+             rocprofv3 counter summary when it matches the current kernel
+             source, else null,
+  cpu_baseline  the CPU oracle's fp32 mirror timed on a bounded sample of the
+             same workload, on one thread and on a pool of
+             min(usable CPUs, 16) threads,
+  parity     the timed launches' outputs against the mirror (every token) and
+             the fp64 truth (a sample),
+  sweep      per workload shape and NEXT-row entry point (decode T=1..256,
+             packed vs fp32 routing, residual + RMSNorm, the routing gate,
+             standalone FP8 activation quant in both scale policies, the
+             expert-parallel combine, the all-reduce + RMSNorm share, the
+             packed decoder; for the gate the "H" field holds the expert
+             count E; the first row is an empty kernel): the per-call time
+             of 20 calls captured in a HIP graph and replayed, and
+             host-inclusive event times (warm, cold after a 1 GiB read-only
+             stream through the caches, and 100 back-to-back calls). A marker
+             launch opens each case, so a kernel trace of the run splits
+             into cases; kernel-only durations come from rocprofv3,
   us_per_call  the timed operation on its first T = 1, 2, 4, ..., 8192
              tokens, the plain bf16 finalize of the same tokens at
              T = 256..8192, the decode finalize at T = 1..256, and an empty kernel
              (one wave, no memory access), all per call under HIP-graph
              replay: the empty kernel is the floor under any call's time.
+
+CPU-only modes (--summarize-trace, --summarize-counters,
+--summarize-sweep-counters) turn rocprofv3 output of a run of this script
+into the summaries kept under profiles/.
 """
 from __future__ import annotations
 
