@@ -94,6 +94,20 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def all_sources_hash() -> str:
+    """SHA-256 over every kernel source file of the library and its build
+    script (sorted by name): what the sweep's kernels are built from."""
+    csrc = os.path.join(ROOT, "combine_moe_finalize_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "combine_moe_finalize_amd", "build.py"), "rb") as f:
+        h.update(b"build.py\0" + f.read())
+    return h.hexdigest()
+
+
 def counters_traffic():
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel source."""
@@ -642,7 +656,8 @@ def summarize_trace(trace_csv, bench_json, out_dir, command):
            "row, the empty kernel (one wave, no memory access), is the floor under every other "
            "row, in the same states.", "",
            f"Kernel source SHA-256 (`finalize_kernels.hip` + `device_common.h` + "
-           f"`moef_internal.h`): `{srcs}`", "",
+           f"`moef_internal.h`): `{srcs}`; every kernel source and the build script: "
+           f"`{line.get('all_sources_sha256', 'not recorded')}`", "",
            "| case | kernel | grid | warm n | warm median µs | p10 | p90 | cold n | cold median µs "
            "| graph µs/call | algorithmic bytes | GB/s warm | GB/s cold | GB/s graph |",
            "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -813,7 +828,8 @@ def summarize_sweep_counters(bench_json, counter_csvs, out_dir, commands, trace_
             "its warm-up, back-to-back, cold (after a 1 GiB read-only flush), batched and "
             "graph-replayed calls; each figure is the mean per call over all of them.", "",
             f"Kernel source SHA-256 (`finalize_kernels.hip` + `device_common.h` + "
-            f"`moef_internal.h`): `{srcs}`", ""]
+            f"`moef_internal.h`): `{srcs}`; every kernel source and the build script: "
+            f"`{line.get('all_sources_sha256', 'not recorded')}`", ""]
     written = {}
     if "FETCH_SIZE" in names and "WRITE_SIZE" in names:
         per = {}
@@ -1057,6 +1073,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "kernel_source_sha256": kernel_source_hash(),
+        "all_sources_sha256": all_sources_hash(),
         "config": {"workload": "prefill_finalize_fp8_ue8m0", "tokens": T, "hidden": H,
                    "experts": wl.E, "top_k": k, "padded_rows": wl.P,
                    "routed_scaling_factor": wl.rsf, "shared_expert": True,
