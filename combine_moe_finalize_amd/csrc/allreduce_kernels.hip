@@ -224,7 +224,7 @@ hipError_t launch_allreduce_rmsnorm(const uint16_t* const* rank_outputs, int32_t
   u32x4* nm = reinterpret_cast<u32x4*>(normed);
   const int nch = (h8 + kWaveLanes - 1) / kWaveLanes;
   const int ncu = device_cus(stream);
-  if (ncu > 0 && tokens * nch >= kStagedRmsFromUnitsPerCu * ncu) {
+  if (ncu > 0 && tokens * nch >= kStagedArFromUnitsPerCu * ncu) {
     const StagedPlan plan = plan_staged(tokens, ncu, kStageRmsUnits / nch);
     return dispatch_ranks(num_ranks, [&](auto rm, auto ex) {
       constexpr int RM = decltype(rm)::value;

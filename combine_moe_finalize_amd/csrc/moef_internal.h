@@ -163,6 +163,11 @@ inline StagedPlan plan_staged_tokens(int64_t tokens, int64_t nchunks, int ncu, i
 constexpr int kStageRmsUnitBytes = kChunkCols * 2 + 8;
 constexpr int kStageRmsUnits = (kLdsPerCu - 256) / kStageRmsUnitBytes;     // 158
 constexpr int64_t kStagedRmsFromUnitsPerCu = 40;
+// The all-reduce + RMSNorm share stages the same way from
+// kStagedArFromUnitsPerCu units per CU (R = 8, H = 7168, kernel-trace
+// medians, one workgroup per token -> staged: T = 256 7.20 -> 7.64 us;
+// 384 10.16 -> 9.80; 512 12.88 -> 11.48; 640 16.44 -> 15.64).
+constexpr int64_t kStagedArFromUnitsPerCu = 20;
 static_assert(kStageRmsUnits * kStageRmsUnitBytes + 4 <= kLdsPerCu, "staging fits the LDS");
 static_assert(kStageRmsUnits / (MOEF_MAX_HIDDEN_RMSNORM / kChunkCols) >= 1,
               "a workgroup holds at least one token of the largest hidden size");

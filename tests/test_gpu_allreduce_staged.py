@@ -1,6 +1,6 @@
 """GPU parity of the staged path of the all-reduce + residual + RMSNorm step.
 
-From 40 (token, 512-column chunk) units per CU the step runs one workgroup
+From 20 (token, 512-column chunk) units per CU the step runs one workgroup
 per CU that owns whole tokens, takes their units from an LDS counter, keeps
 each unit's residual_out vector and chunk sum of squares in LDS (158 units a
 workgroup) and writes residual_out and normed after its last read; grids
@@ -21,7 +21,7 @@ from test_gpu_allreduce import check
 
 pytestmark = pytest.mark.gpu
 
-STAGED_FROM_UNITS_PER_CU = 40
+STAGED_FROM_UNITS_PER_CU = 20
 
 
 @pytest.fixture(scope="module", autouse=True)
