@@ -37,9 +37,11 @@
  *  - All tensor pointers are DEVICE pointers owned by the caller, row-major
  *    and contiguous. bf16 values travel as raw bits in uint16_t, FP8 E4M3
  *    codes and UE8M0 scale bytes as uint8_t. The library never allocates,
- *    frees or keeps a pointer after the call returns, holds no mutable global
- *    state, never synchronizes and never reads device memory from the host,
- *    so every call may be captured into a HIP graph.
+ *    frees or keeps a pointer after the call returns, never synchronizes and
+ *    never reads device memory from the host, so every call may be captured
+ *    into a HIP graph. Its only global state is a per-device cache of the
+ *    CU count (queried on first use, then read); calls on any streams and
+ *    threads may run at once.
  *  - `stream` is a hipStream_t passed as void* (NULL: the null stream). Work
  *    is enqueued on it; the call returns without waiting.
  *  - Return value: MOEF_OK (0) or a MOEF_ERR_* status. Every argument check
