@@ -201,7 +201,8 @@ def test_sweep_counter_summary(tmp_path, monkeypatch):
 
 
 def test_trace_summary(tmp_path, monkeypatch):
-    """The headline's timed launches follow its warm-up ones; a sweep case is
+    """The headline's timed launches follow its warm-up ones, and the steady
+    state is the last 100 of the 300 launches after them; a sweep case is
     split at its marker into warm dispatches, cold ones (right after the
     flush kernel) and the last 200 (the graph replays)."""
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h" * 64)
@@ -210,6 +211,7 @@ def test_trace_summary(tmp_path, monkeypatch):
     mark = "void (anonymous namespace)::empty_probe_kernel()"
     flush = "void (anonymous namespace)::read_probe_kernel(uint4 const*, unsigned int*)"
     d = [(head, 616 * 1024, 180.0)] + [(head, 616 * 1024, us) for us in (170.0, 172.0)]
+    d += [(head, 616 * 1024, 175.0)] * 200 + [(head, 616 * 1024, 168.0)] * 100   # steady state
     d += [(mark, 128, 1.0)] + [(dec, 512, 3.0)] * 30
     d += [(flush, 1 << 26, 150.0), (dec, 512, 5.0)] * 3 + [(dec, 512, 2.0)] * 200
     lines = ["Kernel_Name,Grid_Size_X,Workgroup_Size_X,Dispatch_Id,Start_Timestamp,End_Timestamp"]
@@ -222,6 +224,7 @@ def test_trace_summary(tmp_path, monkeypatch):
             "roofline": {"kernel": "finalize_quant_staged_kernel<8, true, 12> launches=1 "
                                    "grid=616x1024 groups=8 tail=5%",
                          "algorithmic_bytes_per_launch": 1_116_667_904, "kernel_us_avg": 171.5},
+            "steady_state": {"kernel_us_avg": 168.5},
             "sweep": [{"case": "decode", "T": 1, "H": 4096, "top_k": 8,
                        "algorithmic_bytes": 81_984,
                        "kernel": "finalize_kernel<8, true> launches=1 grid=2x256"}]}
@@ -233,3 +236,4 @@ def test_trace_summary(tmp_path, monkeypatch):
     assert out[0]["warm"]["n"] == 230 and out[0]["graph_us_per_call"] == pytest.approx(2.0)
     text = (tmp_path / "prefill_quant_T8192_H7168_kernel_trace.md").read_text()
     assert "| 2 timed (after 1 warm-up) | 171.000 |" in text and "cmd" in text
+    assert "| 100 steady state (the last of 300 launches right after the timed ones) | 168.000 |" in text
