@@ -3,8 +3,8 @@
 // Each entry point validates every argument before it makes any HIP runtime
 // call (so a rejected call enqueues nothing and the checks run on a machine
 // without a GPU), then launches on the caller's stream and returns without
-// synchronizing. The library allocates nothing and keeps no state, so a call
-// can be captured into a HIP graph (the pages size their workspaces before
+// synchronizing. The library allocates nothing and keeps no state beyond a
+// per-device cache of the CU count, so a call can be captured into a HIP graph (the pages size their workspaces before
 // graph capture and never grow them inside: "[Kimi K2.5] Fuse deferred MoE
 // finalize into next-layer AR + residual + RMSNorm", Key modifications).
 
