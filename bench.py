@@ -406,14 +406,14 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
 
     measure("empty kernel (launch floor)", 0, 0, 0, 0, lambda: P.moef_probe_empty(stream()),
             iters_small, kernel="empty_probe_kernel", write_bytes=0)
-    wl = W.config_workload(0)
+    wl = W.family_workload("tiny")
     kw, _ = upload(wl, torch)
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
     measure("tiny", wl.T, wl.H, wl.top_k, bytes_plain(wl.T, wl.H, wl.top_k),
             lambda: M.moe_finalize(**kw, out=out), iters_small,
             kernel=describe(M.OP_FINALIZE, wl.T, wl.H, wl.top_k), write_bytes=wl.T * wl.H * 2)
-    for T in W.CONFIGS[1]["Ts"]:
-        wl = W.config_workload(1, T)
+    for T in W.FAMILIES["decode_sweep"]["Ts"]:
+        wl = W.family_workload("decode_sweep", T)
         kw, _ = upload(wl, torch)
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
         measure("decode", T, wl.H, wl.top_k, bytes_plain(T, wl.H, wl.top_k),
@@ -426,7 +426,7 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
         measure("decode_H7168_E384", T, wl.H, wl.top_k, bytes_plain(T, wl.H, wl.top_k),
                 lambda: M.moe_finalize(**kw, out=out), iters_small,
                 kernel=describe(M.OP_FINALIZE, T, wl.H, wl.top_k), write_bytes=T * wl.H * 2)
-    wl = W.config_workload(2)
+    wl = W.family_workload("packed_vs_unpacked")
     for packed in (False, True):
         kw, _ = upload(wl, torch, packed=packed)
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
@@ -434,8 +434,8 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
                 bytes_plain(wl.T, wl.H, wl.top_k), lambda: M.moe_finalize(**kw, out=out),
                 iters_small, kernel=describe(M.OP_FINALIZE, wl.T, wl.H, wl.top_k),
                 write_bytes=wl.T * wl.H * 2)
-    for T in W.CONFIGS[3]["Ts"]:
-        wl = W.config_workload(3, T)
+    for T in W.FAMILIES["residual_rmsnorm"]["Ts"]:
+        wl = W.family_workload("residual_rmsnorm", T)
         kw, ex = upload(wl, torch)
         ro = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda:0")
         nm = torch.empty_like(ro)
@@ -492,7 +492,7 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
                 iters_big if T >= 2048 else iters_small, write_bytes=2 * T * H * 2)
         del ranks, ares, aro, anm
     n = 8192 * 8
-    pk = torch.from_numpy(W.config_workload(0).packed.reshape(-1).repeat(n // 2)).to("cuda:0")
+    pk = torch.from_numpy(W.family_workload("tiny").packed.reshape(-1).repeat(n // 2)).to("cuda:0")
     ids = torch.empty_like(pk)
     wts = torch.empty(pk.shape, dtype=torch.float32, device="cuda:0")
     measure("packed_decode", 8192, 0, 8, 12 * n,
@@ -1056,7 +1056,7 @@ def main():
     M.load_library()   # fails loudly when the HIP library is missing
 
     t0 = time.perf_counter()
-    wl = W.config_workload(4)
+    wl = W.family_workload("prefill_fp8_ue8m0")
     log(f"generated workload T={wl.T} H={wl.H} k={wl.top_k} P={wl.P} in "
         f"{time.perf_counter() - t0:.1f} s")
     kw, _ = upload(wl, torch)

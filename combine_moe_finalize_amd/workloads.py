@@ -26,7 +26,7 @@ Recipe (every array is a deterministic function of the seed):
     bf16(U(0.5, 1.5)) [H];
   * packed routing: (expert_id << 16) | bf16_bits(weight), the bf16 cast
     being torch's round-to-nearest-even.
-Seeds default to 20261202 + 1000 * config + T.
+Seeds default to 20261202 + 1000 * (the family's seed offset) + T.
 """
 from __future__ import annotations
 
@@ -228,29 +228,32 @@ def activations(T: int, H: int, seed: int, log2_mag: Optional[tuple] = (-8.0, 8.
     return _bf16_normal_matrix(seed, 7, T, H, scale)
 
 
-# The five synthetic workload families (sizes as in the published setup).
-CONFIGS = {
-    0: dict(name="tiny", Ts=(1,), H=1024, E=16, top_k=2),
-    1: dict(name="decode_sweep", Ts=(1, 4, 8, 16, 64, 256), H=4096, E=256, top_k=8),
-    2: dict(name="packed_vs_unpacked", Ts=(256,), H=7168, E=256, top_k=8),
-    3: dict(name="residual_rmsnorm", Ts=(16, 256, 1024), H=7168, E=256, top_k=8),
-    4: dict(name="prefill_fp8_ue8m0", Ts=(8192,), H=7168, E=256, top_k=8),
+# The synthetic workload families (sizes as in the published setup), each
+# with the offset of its default seed.
+FAMILIES = {
+    "tiny": dict(Ts=(1,), H=1024, E=16, top_k=2, seed_offset=0),
+    "decode_sweep": dict(Ts=(1, 4, 8, 16, 64, 256), H=4096, E=256, top_k=8, seed_offset=1),
+    "packed_vs_unpacked": dict(Ts=(256,), H=7168, E=256, top_k=8, seed_offset=2),
+    "residual_rmsnorm": dict(Ts=(16, 256, 1024), H=7168, E=256, top_k=8, seed_offset=3,
+                             with_residual=True),
+    "prefill_fp8_ue8m0": dict(Ts=(8192,), H=7168, E=256, top_k=8, seed_offset=4,
+                              log2_mag=(-8.0, 8.0)),
 }
 
 
-def default_seed(config: int, T: int) -> int:
-    return 20261202 + 1000 * config + T
+def default_seed(seed_offset: int, T: int) -> int:
+    return 20261202 + 1000 * seed_offset + T
 
 
-def config_workload(config: int, T: Optional[int] = None,
+def family_workload(family: str, T: Optional[int] = None,
                     seed: Optional[int] = None) -> Workload:
-    """Workload of a numbered family at token count T (default: its first)."""
-    c = CONFIGS[config]
+    """Workload of a named family at token count T (default: its first)."""
+    c = FAMILIES[family]
     T = c["Ts"][0] if T is None else T
-    seed = default_seed(config, T) if seed is None else seed
-    kw = dict(rsf=2.5, seed=seed, name=f"{c['name']}_T{T}")
-    if config == 3:
+    seed = default_seed(c["seed_offset"], T) if seed is None else seed
+    kw = dict(rsf=2.5, seed=seed, name=f"{family}_T{T}")
+    if c.get("with_residual"):
         kw["with_residual"] = True
-    if config == 4:
-        kw["log2_mag"] = (-8.0, 8.0)
+    if "log2_mag" in c:
+        kw["log2_mag"] = c["log2_mag"]
     return make_workload(T, c["H"], c["E"], c["top_k"], **kw)

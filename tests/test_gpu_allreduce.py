@@ -97,7 +97,7 @@ def test_expert_parallel_chain_on_one_gpu():
     """Each of R ranks finalizes its own slots on the GPU (rank 0 adds the
     shared output); the all-reduce + residual + RMSNorm sums them. Every step
     is compared with the oracle's same chain."""
-    wl = W.config_workload(3, 64)
+    wl = W.family_workload("residual_rmsnorm", 64)
     R = 4
     g2, w = d_bf16(wl.gemm2_out), d_f32(wl.weights)
     announce(f"allreduce EP chain R={R} T={wl.T} H={wl.H}")

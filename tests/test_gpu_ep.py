@@ -49,7 +49,7 @@ def expert_row_starts(wl):
 
 @pytest.mark.parametrize("R", [2, 4, 8])
 def test_ep_chain_on_one_gpu(R):
-    wl = W.config_workload(2)
+    wl = W.family_workload("packed_vs_unpacked")
     starts = expert_row_starts(wl)
     per = wl.E // R
     g2 = d_bf16(wl.gemm2_out)

@@ -50,10 +50,10 @@ def check_finalize(wl, got, packed=False, with_shared=True, what=""):
     return assert_bf16_within_tolerance(got, truth, terms, wl.top_k + 2, what)
 
 
-# ---------------------------------------------------------------- configs
+# ------------------------------------------------------- workload families
 @pytest.mark.parametrize("packed", [False, True])
-def test_tiny_config(packed):
-    wl = W.config_workload(0)
+def test_tiny_workload(packed):
+    wl = W.family_workload("tiny")
     announce(f"tiny T=1 H=1024 k=2 packed={packed}")
     got = run_finalize(wl, packed=packed)
     check_finalize(wl, got, packed=packed, what="tiny")
@@ -62,7 +62,7 @@ def test_tiny_config(packed):
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("T", [1, 4, 8, 16, 64, 256])
 def test_decode_sweep(T, packed):
-    wl = W.config_workload(1, T)
+    wl = W.family_workload("decode_sweep", T)
     announce(f"decode sweep T={T} H=4096 k=8 packed={packed}")
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     got = run_finalize(wl, packed=packed, err=err)
@@ -72,7 +72,7 @@ def test_decode_sweep(T, packed):
 
 
 def test_packed_vs_unpacked_full_size():
-    wl = W.config_workload(2)
+    wl = W.family_workload("packed_vs_unpacked")
     announce("packed vs unpacked T=256 H=7168 k=8")
     up = run_finalize(wl, packed=False)
     pk = run_finalize(wl, packed=True)
@@ -91,7 +91,7 @@ def test_packed_vs_unpacked_full_size():
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("T", [16, 256, 1024])
 def test_residual_rmsnorm(T, packed):
-    wl = W.config_workload(3, T)
+    wl = W.family_workload("residual_rmsnorm", T)
     announce(f"residual+rmsnorm T={T} H=7168 k=8 packed={packed}")
     kw = device_inputs(wl, packed=packed)
     ro, nm = M.moe_finalize_residual_rmsnorm(**kw, residual=d_bf16(wl.residual),
@@ -130,7 +130,7 @@ def check_rmsnorm(wl, ro, nm, packed=False):
 
 @pytest.fixture(scope="module")
 def prefill_workload():
-    return W.config_workload(4)
+    return W.family_workload("prefill_fp8_ue8m0")
 
 
 @pytest.mark.parametrize("packed", [False, True])
@@ -317,7 +317,7 @@ def test_padding_row_reference_is_visible():
 
 
 def test_no_shared_and_rsf_one():
-    wl = W.config_workload(1, 16)
+    wl = W.family_workload("decode_sweep", 16)
     wl.rsf = 1.0
     announce("no shared, rsf 1")
     got = run_finalize(wl, with_shared=False)
@@ -351,7 +351,7 @@ def test_rmsnorm_shapes(H, k):
 
 
 def test_rmsnorm_in_place_residual():
-    wl = W.config_workload(3, 16)
+    wl = W.family_workload("residual_rmsnorm", 16)
     announce("rmsnorm in place")
     kw = device_inputs(wl)
     res = d_bf16(wl.residual)
@@ -378,7 +378,7 @@ def test_packed_decode():
 def test_layout_invariance_on_gpu():
     """The same rows in another order (token-ordered instead of expert-sorted,
     no padding), with the map updated, give bitwise the same output."""
-    wl = W.config_workload(2)
+    wl = W.family_workload("packed_vs_unpacked")
     announce("layout invariance T=256 H=7168")
     a = run_finalize(wl)
     wl.gemm2_out = wl.gemm2_out[wl.idx.reshape(-1)]
@@ -390,7 +390,7 @@ def test_layout_invariance_on_gpu():
 
 # -------------------------------------------------------------- robustness
 def test_deterministic_and_canaries():
-    wl = W.config_workload(1, 64)
+    wl = W.family_workload("decode_sweep", 64)
     announce("determinism and canaries")
     kw = device_inputs(wl)
     T, H = wl.T, wl.H
@@ -408,7 +408,7 @@ def test_deterministic_and_canaries():
 
 
 def test_graph_capture_replay():
-    wl = W.config_workload(1, 16)
+    wl = W.family_workload("decode_sweep", 16)
     announce("graph capture")
     kw = device_inputs(wl)
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=DEV)

@@ -52,7 +52,7 @@ def same(a, b):
 
 def entry_points():
     """(name, fn writing into its outputs, outputs, buffers) per entry point."""
-    wl = W.config_workload(1, 16)
+    wl = W.family_workload("decode_sweep", 16)
     wr = W.make_workload(8, 7168, 64, 8, rsf=2.5, seed=3, with_residual=True)
     cases = []
 

@@ -243,7 +243,7 @@ def test_wide_layout_at_capacity(ncu):
 def test_wide_layout_prefill_shape(ncu):
     """The prefill shape the wide layout exists for (T = 8192, H = 7168,
     top_k = 8: 448 units per CU on 256 CUs, one launch), against the mirror."""
-    wl = W.config_workload(4)
+    wl = W.family_workload("prefill_fp8_ue8m0")
     announce(f"staged finalize, prefill T={wl.T} H={wl.H} (wide layout from "
              f"{(LDS_UNITS + REG_UNITS_PER_CU) * ncu} units)")
     got = run_plain(wl)

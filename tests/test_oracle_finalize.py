@@ -109,8 +109,8 @@ def test_golden_ue8m0_quant():
 
 
 # -------------------------------------------------- exact rational brute force
-def test_config0_truth_equals_exact_rational():
-    wl = W.config_workload(0)
+def test_tiny_workload_truth_equals_exact_rational():
+    wl = W.family_workload("tiny")
     out, flag = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
                                  shared=wl.shared, rsf=wl.rsf)
     assert flag == 0
@@ -171,8 +171,8 @@ def test_identical_rows_reproduce_the_row(mode):
 
 
 def test_nan_padding_never_reaches_output():
-    for cfg, T in [(0, 1), (1, 16), (2, 256)]:
-        wl = W.config_workload(cfg, T)
+    for fam, T in [("tiny", 1), ("decode_sweep", 16), ("packed_vs_unpacked", 256)]:
+        wl = W.family_workload(fam, T)
         assert np.isnan(F.bf16_to_f64(wl.gemm2_out)).any()   # padding exists
         out, flag = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
                                      shared=wl.shared, rsf=wl.rsf)
@@ -180,7 +180,7 @@ def test_nan_padding_never_reaches_output():
 
 
 def test_rsf_one_is_neutral_and_scales_only_routed():
-    wl = W.config_workload(1, 8)
+    wl = W.family_workload("decode_sweep", 8)
     a, _ = O.finalize_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
                              shared=wl.shared, rsf=1.0)
     # rsf = 1.0 equals the definition with the raw fp32 weights
@@ -204,7 +204,7 @@ def test_rsf_one_is_neutral_and_scales_only_routed():
 
 @pytest.mark.parametrize("mode", ["truth", "mirror"])
 def test_doubling_is_exact(mode):
-    wl = W.config_workload(1, 4)
+    wl = W.family_workload("decode_sweep", 4)
     fn = O.finalize_truth if mode == "truth" else O.finalize_mirror
     a, _ = fn(wl.gemm2_out, wl.idx, weights_f32=wl.weights, shared=wl.shared, rsf=1.25)
     sh2 = W.to_bf16_bits(2 * F.bf16_to_f32(wl.shared))
@@ -214,7 +214,7 @@ def test_doubling_is_exact(mode):
 
 @pytest.mark.parametrize("mode", ["truth", "mirror"])
 def test_packed_equals_bf16_rounded_unpacked(mode):
-    wl = W.config_workload(2)
+    wl = W.family_workload("packed_vs_unpacked")
     fn = O.finalize_truth if mode == "truth" else O.finalize_mirror
     wl_sub = slice(0, 64)
     idx = wl.idx[wl_sub]
@@ -310,7 +310,7 @@ def test_rank_with_no_rows():
 
 
 def test_mirror_within_two_ulp_of_truth():
-    wl = W.config_workload(1, 64)
+    wl = W.family_workload("decode_sweep", 64)
     m, _ = O.finalize_mirror(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
                              shared=wl.shared, rsf=wl.rsf)
     t, _ = O.finalize_truth(wl.gemm2_out, wl.idx, weights_f32=wl.weights,
@@ -324,7 +324,7 @@ def test_mirror_within_two_ulp_of_truth():
 
 # ---------------------------------------------------------- residual + RMSNorm
 def test_residual_out_is_single_rounding_of_shared_like_term():
-    wl = W.config_workload(3, 16)
+    wl = W.family_workload("residual_rmsnorm", 16)
     ro, _, _ = O.finalize_residual_rmsnorm_truth(
         wl.gemm2_out, wl.idx, weights_f32=wl.weights, shared=None, rsf=wl.rsf,
         residual=wl.residual, gamma=wl.gamma, eps=wl.eps)
@@ -351,7 +351,7 @@ def test_residual_out_exact_rational_tiny():
 
 
 def test_rmsnorm_matches_torch_rms_norm():
-    wl = W.config_workload(3, 16)
+    wl = W.family_workload("residual_rmsnorm", 16)
     ro, normed, _ = O.finalize_residual_rmsnorm_truth(
         wl.gemm2_out, wl.idx, weights_f32=wl.weights, shared=wl.shared, rsf=wl.rsf,
         residual=wl.residual, gamma=wl.gamma, eps=wl.eps)

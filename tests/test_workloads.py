@@ -50,8 +50,8 @@ def test_routing_distinct_and_normalised():
     assert np.all(wl.weights > 0)
 
 
-def test_config_shapes_and_magnitudes():
-    wl = W.config_workload(0)
+def test_family_shapes_and_magnitudes():
+    wl = W.family_workload("tiny")
     assert (wl.T, wl.H, wl.E, wl.top_k, wl.rsf) == (1, 1024, 16, 2, 2.5)
     assert wl.shared.shape == (1, 1024) and wl.idx.dtype == np.int32
     assert wl.P % 128 == 0
