@@ -13,7 +13,9 @@ UE8M0 / E4M3 quantization.
 Printed: one JSON line with
   value      algorithmic GB/s of the whole step (bytes the method must move /
              wall time per step, inputs resident),
-  kernel_source_sha256  the finalize kernel sources the run used,
+  kernel_source_sha256  the finalize kernel sources the run used
+             (all_sources_sha256: every kernel source and header and the
+             build script),
   ceilings   same-session streaming read and copy rates (the bandwidth probe
              kernels) and torch's device copy, with the headline kernel's rate
              as a fraction of the read and copy rates (the kernel moves 95%
