@@ -353,12 +353,13 @@ def probe_lib():
     return P
 
 
-def sweep(torch, M, W, iters_small=200, iters_big=50):
+def sweep(torch, M, W, iters_small=700, iters_big=100):
     """Every workload shape and NEXT-row entry point. Before each case the
     probe library's marker kernel (the empty kernel on two workgroups) is
     launched, so a kernel trace of this run splits into one block per case,
-    in the order of the returned rows. A case's dispatches: 5 warm-up calls,
-    `iters` back-to-back event-timed calls (warm), iters / 10 calls each
+    in the order of the returned rows. A case's dispatches: 10 warm-up calls,
+    `iters` back-to-back event-timed calls (warm; 700 for the decode-size
+    cases, 100 for the prefill-size ones), iters / 10 calls each
     after a 1 GiB read-only stream through the caches (cold), 100
     back-to-back calls, and 20 calls captured in a HIP graph and replayed.
     The read-only flush leaves no dirty lines behind, so a cold call is not
@@ -381,7 +382,7 @@ def sweep(torch, M, W, iters_small=200, iters_big=50):
         if P.moef_probe_mark(stream()) != 0:
             raise RuntimeError("marker launch failed")
         torch.cuda.synchronize()
-        for _ in range(5):
+        for _ in range(10):
             fn()
         warm = event_times_us(torch, fn, iters)
         cold = event_times_us(torch, fn, max(10, iters // 10), flush=flush)
@@ -692,7 +693,7 @@ def summarize_trace(trace_csv, bench_json, out_dir, command):
            "Same run and command as `prefill_quant_T8192_H7168_kernel_trace.md`:", "",
            f"    {command}", "",
            "Written by `python bench.py --summarize-trace`. Each sweep case starts with a marker "
-           "launch; its dispatches are 5 warm-up calls, back-to-back calls, calls each after a "
+           "launch; its dispatches are 10 warm-up calls, back-to-back calls, calls each after a "
            "1 GiB read-only stream through the caches (**cold**: the dispatch right after the "
            "flush kernel), 100 back-to-back calls and 20-call HIP-graph replays. **Warm** is "
            "every dispatch of the case's kernel that does not follow a flush; **graph** is the "
@@ -1006,7 +1007,7 @@ def summarize_sweep_counters(bench_json, counter_csvs, out_dir, commands, trace_
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
