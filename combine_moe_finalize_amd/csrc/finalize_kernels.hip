@@ -1067,7 +1067,7 @@ hipError_t launch_ep_combine(const uint16_t* partials, int32_t num_partials,
                              int64_t hidden, hipStream_t stream) {
   const int64_t n = tokens * (hidden / kVecElems);
   const unsigned int blocks = (unsigned int)((n + 255) / 256);
-  const size_t lds = stream_cap_lds(((int64_t)blocks * 256) / kWaveLanes);
+  const size_t lds = ep_cap_lds(((int64_t)blocks * 256) / kWaveLanes, num_partials);
   hipLaunchKernelGGL(ep_combine_kernel, dim3(blocks), dim3(256), lds, stream,
                      reinterpret_cast<const u32x4*>(partials), (int)num_partials, n,
                      reinterpret_cast<const u32x4*>(shared), reinterpret_cast<u32x4*>(out), n);

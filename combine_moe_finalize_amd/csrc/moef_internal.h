@@ -79,15 +79,34 @@ constexpr int kLdsPerCu = 160 * 1024;
 constexpr size_t lds_for_blocks_per_cu(int blocks) {
   return (size_t)((kLdsPerCu / (blocks + 1) + 512) / 512 * 512);
 }
-// The finalize kernels with one wave per (token, chunk) and the EP combine
-// hold at most 4 of their 4-wave workgroups (16 waves) per CU once a grid is
-// twice what fits on the chip uncapped (16384 waves): fewer waves streaming
-// at once lose less to reads and writes mixing at the DRAM. (The act-quant
-// kernels measured slower with any cap and run uncapped.)
+// The finalize kernels with one wave per (token, chunk) hold at most 4 of
+// their 4-wave workgroups (16 waves) per CU once a grid is twice what fits
+// on the chip uncapped (16384 waves): fewer waves streaming at once lose
+// less to reads and writes mixing at the DRAM. (The act-quant kernels
+// measured slower with any cap and run uncapped.)
 constexpr int kStreamCapBlocksPerCu = 4;
 constexpr int64_t kStreamCapFromWaves = 16384;
 constexpr size_t stream_cap_lds(int64_t waves) {
   return waves >= kStreamCapFromWaves ? lds_for_blocks_per_cu(kStreamCapBlocksPerCu) : 0;
+}
+// The EP combine's cap follows its partial count R. A thread loads the
+// ranks four at a time and the last R % 4 of them one at a time, so with
+// few partials it has few loads in flight and more workgroups per CU keep
+// the memory system busy: none for R = 1 (kEpCapNone: no reservation, the
+// register-bound occupancy of 8), 7 for R = 2, 5 for R = 3, and the
+// finalize kernels' 4 from R = 4. Kernel-trace medians against a fixed cap
+// of 4 (µs, H = 7168): T = 8192, R = 1 / 2 / 3: 62.1 / 84.0 / 107.9 ->
+// 54.1 / 75.6 / 94.0; R = 2 at T = 4096 and 2048: 41.8 -> 38.5, 21.6 ->
+// 20.0. Caps of 3 or 5-7 from R = 4 on were no better across sizes (3 gains
+// 2-3% at T = 8192 for R = 8 and 16 but loses 1-3% at T = 2048-4096).
+constexpr int kEpCapNone = 8;
+constexpr int ep_cap_blocks(int partials) {
+  return partials <= 1 ? kEpCapNone : partials == 2 ? 7 : partials == 3 ? 5 : kStreamCapBlocksPerCu;
+}
+constexpr size_t ep_cap_lds(int64_t waves, int partials) {
+  return waves >= kStreamCapFromWaves && ep_cap_blocks(partials) < kEpCapNone
+             ? lds_for_blocks_per_cu(ep_cap_blocks(partials))
+             : 0;
 }
 // The UE8M0 finalize on large grids stages its output on chip and writes it
 // after the gathers (finalize_quant_staged_kernel): one workgroup of
@@ -318,6 +337,9 @@ int device_cus(hipStream_t stream);
 // waves per CU (5 per SIMD): measured faster at large T than the 24 its
 // register use would allow.
 constexpr int kNorm2MaxWavesPerCu = 20;
+static_assert(lds_for_blocks_per_cu(5) * 5 <= kLdsPerCu && lds_for_blocks_per_cu(5) * 6 > kLdsPerCu &&
+              lds_for_blocks_per_cu(7) * 7 <= kLdsPerCu && lds_for_blocks_per_cu(7) * 8 > kLdsPerCu,
+              "EP combine cap reservations");
 static_assert(lds_for_blocks_per_cu(kStreamCapBlocksPerCu) * kStreamCapBlocksPerCu <= kLdsPerCu &&
               lds_for_blocks_per_cu(kStreamCapBlocksPerCu) * (kStreamCapBlocksPerCu + 1) > kLdsPerCu &&
               lds_for_blocks_per_cu(kStreamCapBlocksPerCu) <= 65536, "cap reservation");
