@@ -92,13 +92,13 @@ constexpr size_t stream_cap_lds(int64_t waves) {
 // The EP combine's cap follows its partial count R. A thread loads the
 // ranks four at a time and the last R % 4 of them one at a time, so with
 // few partials it has few loads in flight and more workgroups per CU keep
-// the memory system busy: none for R = 1 (kEpCapNone: no reservation, the
-// register-bound occupancy of 8), 7 for R = 2, 5 for R = 3, and the
-// finalize kernels' 4 from R = 4. Kernel-trace medians against a fixed cap
-// of 4 (µs, H = 7168): T = 8192, R = 1 / 2 / 3: 62.1 / 84.0 / 107.9 ->
-// 54.1 / 75.6 / 94.0; R = 2 at T = 4096 and 2048: 41.8 -> 38.5, 21.6 ->
-// 20.0. Caps of 3 or 5-7 from R = 4 on were no better across sizes (3 gains
-// 2-3% at T = 8192 for R = 8 and 16 but loses 1-3% at T = 2048-4096).
+// the memory system busy: no reservation for R = 1 (kEpCapNone: 8 of its
+// 4-wave workgroups, the 32 wave slots of a CU), 7 for R = 2, 5 for R = 3,
+// and the finalize kernels' 4 from R = 4. Kernel-trace medians against a
+// fixed cap of 4 (µs, H = 7168): T = 8192, R = 1 / 2 / 3: 62.1 / 84.0 /
+// 107.9 -> 54.1 / 75.6 / 94.0; R = 2 at T = 4096 and 2048: 41.8 -> 38.5,
+// 21.6 -> 20.0. Caps of 3 or 5-7 from R = 4 on were no better across sizes
+// (3 gains 2-3% at T = 8192 for R = 8 and 16 but loses 1-3% at T = 2048-4096).
 constexpr int kEpCapNone = 8;
 constexpr int ep_cap_blocks(int partials) {
   return partials <= 1 ? kEpCapNone : partials == 2 ? 7 : partials == 3 ? 5 : kStreamCapBlocksPerCu;
